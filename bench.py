@@ -1,0 +1,206 @@
+"""Benchmark of the codec's hot path on one MI355X.
+
+One step = one pass over every stage of the path on resident synthetic data:
+  1. quantize the prefill chunk (64 layers x 8192 tokens x 8 kv-heads,
+     head_dim 128, k8v3) into the five planes,
+  2. dequantize the whole chunk back to bf16 K and V,
+  3. fused dequant-on-fetch GQA decode attention over a k8v3 cache of
+     16 sequences x 8 kv-heads x 32768 tokens with 32 query heads.
+`value` is the token-heads quantized per second of the whole step; each stage's
+own throughput and bandwidth are reported under "phases".  Per-kernel times
+come from HIP events recorded on the stream the library launches on.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PREFILL = "prefill_k8v3_d128"
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_quantization_02_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+    if not os.path.exists(path):
+        return None
+    src = source_hash()
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split())
+        if f.get("kernel") == kernel and f.get("src") == src:
+            return float(f["bytes_per_launch"])
+    return None
+
+
+def cpu_baseline(k, v, signs, rows: int):
+    """The oracle as it stands, on the first `rows` rows of the chunk (one core)."""
+    import numpy as np
+    import torch
+
+    from kv_cache_quantization_02_amd import synth
+    from oracle import codec
+    d = k.shape[-1]
+    kk = k.reshape(-1, d)[:rows]
+    vv = v.reshape(-1, d)[:rows]
+    t0 = time.perf_counter()
+    step = 32768
+    for i in range(0, rows, step):
+        kb = synth.bf16_bits(kk[i:i + step])
+        vb = synth.bf16_bits(vv[i:i + step])
+        p = codec.quantize_kv(kb, vb, signs, 8, 3)
+        codec.dequantize_kv(p, signs, d, 8, 3)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "token-heads/s", "cores": 1, "kind": "oracle",
+            "sample": f"quantize + dequantize of the first {rows} token-head rows of the "
+                      f"prefill chunk (k8v3, d128), numpy float32 on one host core, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=262144)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the codec shards by layer or kv-head with no "
+              "communication, so there is no multi-GPU run to time (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_quantization_02_amd import binding as tq
+    from kv_cache_quantization_02_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS[PREFILL]
+    _log(f"generating {PREFILL}: {L}x{T}x{H} rows, d={d}")
+    k, v = synth.kv_inputs(rec, L, T, H, d, seed, device=dev)
+    signs = synth.sign_vector(d)
+    sig = torch.from_numpy(signs).to(dev)
+    sch = tq.scheme(d, kb, vb)
+    planes = tq.alloc_planes(sch, (L, T, H), dev)
+    kout = torch.empty_like(k)
+    vout = torch.empty_like(v)
+    rows_q = L * T * H
+
+    cfg = synth.DECODE_ATTN
+    B, Hq, Hkv, N = cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["context"]
+    _log(f"generating decode cache: {B}x{Hkv}x{N} rows")
+    kc, vc = synth.kv_inputs("normal", B, N, Hkv, d, cfg["seed"], device=dev)
+    cache = tq.quantize_into_cache(kc, vc, sig, cfg["k_bits"], cfg["v_bits"])
+    del kc, vc
+    q = synth.queries(B, Hq, d, cfg["seed"] + 7, device=dev)
+    ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.tq_decode_attn_workspace_bytes(sch, B, Hq, Hkv, N), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    rows_a = B * Hkv * N
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        tq.quantize_kv(k, v, sig, kb, vb, out=planes)
+        if ev: ev[1].record()
+        tq.dequantize_kv(planes, sig, d, kb, vb, k_out=kout, v_out=vout)
+        if ev: ev[2].record()
+        tq.decode_attn(q, cache, ctx, sig, kb, vb, Hkv, out=out, workspace=ws)
+        if ev: ev[3].record()
+
+    _log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    phase_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, name in enumerate(("quantize", "dequantize", "decode_attn"))}
+    _log(f"timed {args.steps} steps: {total_ms:.2f} ms GPU, {wall * 1e3:.2f} ms wall")
+
+    row_bytes = tq.tq_row_bytes(sch)
+    bytes_q = rows_q * (4 * d + row_bytes)          # bf16 K+V read, planes written
+    bytes_dq = rows_q * (row_bytes + 4 * d)         # planes read, bf16 K+V written
+    bytes_a = rows_a * row_bytes + 2 * (2 * B * Hq * d)
+    phases = {
+        "quantize": {"kernel": "quantize_kernel<128,8,3>", "us": phase_ms["quantize"] * 1e3,
+                     "token_heads_per_s": rows_q / (phase_ms["quantize"] * 1e-3),
+                     "GBps": bytes_q / (phase_ms["quantize"] * 1e-3) / 1e9},
+        "dequantize": {"kernel": "dequantize_kernel<128,8,3>", "us": phase_ms["dequantize"] * 1e3,
+                       "token_heads_per_s": rows_q / (phase_ms["dequantize"] * 1e-3),
+                       "GBps": bytes_dq / (phase_ms["dequantize"] * 1e-3) / 1e9},
+        "decode_attn": {"kernel": "decode_attn_split_kernel<128,8,3> + combine",
+                        "us": phase_ms["decode_attn"] * 1e3,
+                        "cache_token_heads_per_s": rows_a / (phase_ms["decode_attn"] * 1e-3),
+                        "GBps": bytes_a / (phase_ms["decode_attn"] * 1e-3) / 1e9},
+    }
+    for p in phases.values():
+        p["frac_of_hbm_peak"] = p["GBps"] / HBM_PEAK_GBS
+    dom = max(phases, key=lambda n: phases[n]["us"])
+    dom_bytes = {"quantize": bytes_q, "dequantize": bytes_dq, "decode_attn": bytes_a}[dom]
+    kname = phases[dom]["kernel"].split("<")[0]
+    roofline = {"bound": "hbm", "achieved": phases[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": phases[dom]["GBps"] / HBM_PEAK_GBS, "traffic": measured_traffic(kname),
+                "kernel": phases[dom]["kernel"], "algorithmic_bytes_per_launch": dom_bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        cpu = cpu_baseline(k, v, signs, args.cpu_rows)
+
+    value = rows_q / (ms_per_step * 1e-3)
+    line = {
+        "metric": "KV token-heads quantized/s and HBM GB/s (% of peak), k8v3 d=128; decode-attn GB/s",
+        "value": value, "unit": "token-heads/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, fp32 arithmetic, k8v3 planes", "data": "synthetic",
+        "config": {"workload": "prefill chunk k8v3 d128 (64 layers x 8192 tokens x 8 kv-heads) quantize "
+                               "+ full dequantize, then fused GQA decode over a 16x8x32768 k8v3 cache "
+                               "with 32 query heads",
+                   "rows_quantized_per_step": rows_q, "decode_cache_rows": rows_a,
+                   "parallelism": "single GPU"},
+        "phases": phases,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) TurboQuant-style KV-cache codec.
+ *
+ * The method is the KV leg of the mlx-bun TurboQuant design pages
+ * ("Algorithm (vllm-metal reference semantics, exact)" on the TurboQuant
+ * page; "Algorithm" on the TurboQuant KV design page).  Per token and per
+ * kv-head, head_dim is split into groups of 32:
+ *   keys   -- no rotation; asymmetric affine per group, fp16 scale and zero;
+ *             signed int8 at 8 bits, packed unsigned at 2/4/5 bits;
+ *   values -- y = FWHT(x * signs) / sqrt(d); per-group RMS scale (fp16);
+ *             Lloyd-Max index of y / (scale + 1e-8); packed bitstream.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All data pointers are DEVICE pointers unless stated; the caller owns
+ *   every buffer.  The library allocates nothing and keeps no mutable
+ *   state; calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ *   default stream) and may be made from several host threads.
+ * - bf16 and fp16 travel as raw 16-bit patterns (uint16_t).
+ * - Rows.  One (token, kv-head) pair is a "row".  A bf16 row is head_dim
+ *   contiguous elements; a plane row is tq_plane_row_bytes() contiguous
+ *   bytes.  tq_rows addresses rows as
+ *       row(s, t, h) = s*seq_stride + t*tok_stride + h*head_stride
+ *   counted in rows of the buffer it describes, so a contiguous
+ *   [L, T, H, d] tensor has (n_seq, n_tok, n_head) = (L, T, H) and strides
+ *   (T*H, H, 1), and a [B, H, N_cap] cache window has strides (H*N_cap, 1, N_cap).
+ * - Alignment: bf16 tensors, the sign vector, the workspace and the query /
+ *   output of the decode call are 16-byte aligned; the packed planes k_q and
+ *   v_q are 8-byte aligned; the fp16 planes are 2-byte aligned.  Plane row
+ *   lengths keep these for any row offset.  Input and output buffers must
+ *   not overlap.
+ * - Validation runs on the host before any launch; on error nothing is
+ *   launched and a negative TQ_E_* code is returned.  Zero rows is a no-op.
+ *   Device faults surface at the caller's next synchronisation.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_OK 0
+#define TQ_E_HEAD_DIM (-1)  /* head_dim not in {64, 128, 256, 512}              */
+#define TQ_E_BITS (-2)      /* k_bits not in {2,4,5,8} or v_bits not in {2,3,4,5,8} */
+#define TQ_E_NULL (-3)      /* a required pointer is NULL                        */
+#define TQ_E_SHAPE (-4)     /* negative count/stride, mismatched counts, Hq % Hkv */
+#define TQ_E_ALIGN (-5)     /* a base pointer breaks the alignment rules below   */
+#define TQ_E_WORKSPACE (-6) /* decode workspace missing or too small             */
+#define TQ_E_HIP (-7)       /* the HIP runtime reported a launch error           */
+#define TQ_E_PLANE (-8)     /* plane index out of range                          */
+
+/* Quantization scheme, validated on every call.  The pages' served sets:
+ * head_dim in {64,128,256,512}; k_bits in {2,4,5,8}; v_bits in {2,3,4,5,8}
+ * (TurboQuant page, "Algorithm" and the scheme list under "Architecture"). */
+typedef struct {
+  int32_t head_dim;
+  int32_t k_bits;
+  int32_t v_bits;
+} tq_scheme;
+
+/* The five planes of a quantized cache, addressed by the same row index.
+ * Per row (d = head_dim, G = d/32):
+ *   k_q     : k_bits == 8 -> int8[d]; else uint8[d*k_bits/8] packed stream
+ *   k_scale : fp16[G]     k_zero : fp16[G]
+ *   v_q     : uint8[d*v_bits/8] packed stream
+ *   v_scale : fp16[G]
+ * Packed streams are little-endian: element i occupies stream bits
+ * [i*b, i*b+b), index LSB first; stream bit n is bit n%8 of byte n/8
+ * (TurboQuant page, "Algorithm", values bullet "Pack"). */
+typedef struct {
+  void* k_q;
+  void* k_scale;
+  void* k_zero;
+  void* v_q;
+  void* v_scale;
+} tq_planes;
+
+enum { TQ_PLANE_K_Q = 0, TQ_PLANE_K_SCALE, TQ_PLANE_K_ZERO, TQ_PLANE_V_Q, TQ_PLANE_V_SCALE };
+
+typedef struct {
+  int64_t n_seq, n_tok, n_head;
+  int64_t seq_stride, tok_stride, head_stride;
+} tq_rows;
+
+/* TQ_OK or TQ_E_HEAD_DIM / TQ_E_BITS for the scheme (host only, pure). */
+int32_t tq_check_scheme(const tq_scheme* scheme);
+
+/* Bytes per row of one plane (TQ_PLANE_*), or a negative TQ_E_* code.
+ * k8v3 at d=128 totals 200 bytes against 512 of bf16 K+V (TurboQuant page,
+ * "Algorithm", bytes paragraph).  Host only, pure. */
+int64_t tq_plane_row_bytes(const tq_scheme* scheme, int32_t plane);
+
+/* Sum of the five planes' row bytes, or a negative TQ_E_* code. */
+int64_t tq_row_bytes(const tq_scheme* scheme);
+
+/* Copies the library's value codebook for `bits` in {1,2,3,4,5,8} into host
+ * arrays: 2^bits ascending float32 centroids and 2^bits - 1 ascending
+ * boundaries.  The 3-bit table is the one the pages print; the others are
+ * the Lloyd-Max fixed points for N(0,1) rounded to float32 (TurboQuant page,
+ * "Algorithm", values bullet).  Host only.  Returns TQ_OK or TQ_E_BITS. */
+int32_t tq_codebook(int32_t bits, float* centroids, float* boundaries);
+
+/* Quantize K and V rows into the five planes.
+ *   k_bf16, v_bf16 : bf16 rows addressed by *in_rows
+ *   signs          : int8[head_dim] of +1/-1, the value sign vector
+ *   out            : planes addressed by *out_rows (same n_seq/n_tok/n_head)
+ * Keys (TurboQuant page, "Algorithm", keys bullets), per 32-group in fp32:
+ *   k_bits = 8      scale = (max-min)/254, zero = round((max+min)/(2 scale)),
+ *                   idx = clip(round(x/scale - zero), -127, 127)
+ *   k_bits in 2,4,5 scale = (max-min)/(2^b-1), zero = round(min/scale),
+ *                   idx = clip(round(x/scale - zero), 0, 2^b-1)
+ *   scale and zero are stored as fp16 after the index is formed.
+ * Values (same section, values bullets): y = FWHT(x*signs)/sqrt(d);
+ *   scale = sqrt(mean(y^2)) per group; idx = #{boundaries < y/(scale+1e-8)}.
+ * Edge semantics: min/max propagate NaN (and order -0 below +0); round is
+ * half-to-even; clip sends NaN to the low end; a constant key group gives
+ * scale 0 and zero +-Inf (NaN for an all-zero group); any NaN stored as
+ * fp16 is 0x7E00.  Returns TQ_OK or a TQ_E_* code. */
+int32_t tq_quantize_kv(const tq_scheme* scheme, const uint16_t* k_bf16, const uint16_t* v_bf16,
+                       const tq_rows* in_rows, const int8_t* signs, const tq_planes* out,
+                       const tq_rows* out_rows, void* stream);
+
+/* Dequantize planes back to bf16 rows (either output may be NULL to skip it).
+ *   keys   : k_hat = (float(idx) + float(zero16)) * float(scale16)
+ *            (f32 add before the multiply; TurboQuant page, packed-value decode
+ *            section on the joint K/V decoder)
+ *   values : signs * FWHT(centroid[idx] * float(scale16)) / sqrt(d), the
+ *            transform first and the signs last (TurboQuant KV design page,
+ *            "Algorithm", dequant bullet)
+ * Outputs round to nearest even; NaN is written as 0x7FC0. */
+int32_t tq_dequantize_kv(const tq_scheme* scheme, const tq_planes* in, const tq_rows* in_rows,
+                         const int8_t* signs, uint16_t* k_bf16, uint16_t* v_bf16,
+                         const tq_rows* out_rows, void* stream);
+
+/* Workspace bytes tq_decode_attn_quant needs for these sizes (host only);
+ * 0 when the arguments are invalid. */
+size_t tq_decode_attn_workspace_bytes(const tq_scheme* scheme, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t max_ctx);
+
+/* Fused dequant-on-fetch GQA decode attention over a quantized cache, one
+ * query per sequence.  For batch b and query head h (kv head
+ * g = h / (n_q_heads / n_kv_heads)):
+ *   s_t = softmax_scale * q . k_hat_t           (t < ctx_lens[b])
+ *   a   = sum_t softmax(s)_t * z_t               z = centroid[idx] * scale16
+ *   out = signs * FWHT(a) / sqrt(d)             (bf16)
+ * i.e. values are accumulated in the rotated domain and un-rotated once per
+ * output row (TurboQuant page, "Deferred inverse FWHT").
+ *   q_bf16    : [batch, n_q_heads, head_dim]
+ *   cache     : planes; row(b, g, t) = b*seq_stride_rows + g*head_stride_rows + t
+ *   ctx_lens  : device int32[batch]; values are clamped to [0, max_ctx] and a
+ *               sequence with 0 tokens gets an all-zero output row
+ *   max_ctx   : cache capacity in tokens (>= 1); sizes the launch
+ *   out_bf16  : [batch, n_q_heads, head_dim]
+ *   workspace : device scratch of >= tq_decode_attn_workspace_bytes() bytes */
+int32_t tq_decode_attn_quant(const tq_scheme* scheme, const uint16_t* q_bf16, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache,
+                             int64_t seq_stride_rows, int64_t head_stride_rows,
+                             const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
+                             const int8_t* signs, uint16_t* out_bf16, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* tq_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

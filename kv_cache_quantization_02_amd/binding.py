@@ -1,0 +1,242 @@
+"""ctypes binding of libtq.so (include/tq.h), with the same entry-point names.
+
+Only argument marshalling happens here: torch supplies device memory and the
+current HIP stream; every step of the codec runs in the library's kernels.
+There is no fallback: if libtq.so cannot be loaded the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+
+TQ_OK = 0
+PLANES = ("k_q", "k_scale", "k_zero", "v_q", "v_scale")
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class Scheme(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32)]
+
+
+class Planes(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in PLANES]
+
+
+class Rows(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("n_seq", "n_tok", "n_head", "seq_stride", "tok_stride", "head_stride")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_quantization_02_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER
+        L.tq_check_scheme.argtypes = [P(Scheme)]
+        L.tq_check_scheme.restype = ctypes.c_int32
+        L.tq_plane_row_bytes.argtypes = [P(Scheme), ctypes.c_int32]
+        L.tq_plane_row_bytes.restype = ctypes.c_int64
+        L.tq_row_bytes.argtypes = [P(Scheme)]
+        L.tq_row_bytes.restype = ctypes.c_int64
+        L.tq_codebook.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        L.tq_codebook.restype = ctypes.c_int32
+        L.tq_quantize_kv.argtypes = [P(Scheme), ctypes.c_void_p, ctypes.c_void_p, P(Rows),
+                                     ctypes.c_void_p, P(Planes), P(Rows), ctypes.c_void_p]
+        L.tq_quantize_kv.restype = ctypes.c_int32
+        L.tq_dequantize_kv.argtypes = [P(Scheme), P(Planes), P(Rows), ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, P(Rows), ctypes.c_void_p]
+        L.tq_dequantize_kv.restype = ctypes.c_int32
+        L.tq_decode_attn_workspace_bytes.argtypes = [P(Scheme), ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.c_int32]
+        L.tq_decode_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.tq_decode_attn_quant.argtypes = [
+            P(Scheme), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(Planes),
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_decode_attn_quant.restype = ctypes.c_int32
+        L.tq_status_string.argtypes = [ctypes.c_int32]
+        L.tq_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tq_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        raise TQError(status, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream
+    if torch.cuda.is_available() and torch.cuda.is_initialized():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+# ----------------------------------------------------------------- raw C ABI
+def tq_check_scheme(scheme: Scheme) -> int:
+    return lib().tq_check_scheme(ctypes.byref(scheme))
+
+
+def tq_plane_row_bytes(scheme: Scheme, plane: int) -> int:
+    return lib().tq_plane_row_bytes(ctypes.byref(scheme), plane)
+
+
+def tq_row_bytes(scheme: Scheme) -> int:
+    return lib().tq_row_bytes(ctypes.byref(scheme))
+
+
+def tq_codebook(bits: int):
+    import numpy as np
+    c = np.zeros(1 << bits, np.float32)
+    b = np.zeros((1 << bits) - 1, np.float32)
+    _check(lib().tq_codebook(bits, c.ctypes.data, b.ctypes.data), "tq_codebook")
+    return c, b
+
+
+def tq_quantize_kv(scheme, k, v, in_rows, signs, out, out_rows, stream=None) -> int:
+    return lib().tq_quantize_kv(ctypes.byref(scheme), _ptr(k), _ptr(v), ctypes.byref(in_rows),
+                                _ptr(signs), ctypes.byref(out), ctypes.byref(out_rows), _stream(stream))
+
+
+def tq_dequantize_kv(scheme, planes, in_rows, signs, k_out, v_out, out_rows, stream=None) -> int:
+    return lib().tq_dequantize_kv(ctypes.byref(scheme), ctypes.byref(planes), ctypes.byref(in_rows),
+                                  _ptr(signs), _ptr(k_out), _ptr(v_out), ctypes.byref(out_rows),
+                                  _stream(stream))
+
+
+def tq_decode_attn_workspace_bytes(scheme, batch, n_q_heads, n_kv_heads, max_ctx) -> int:
+    return lib().tq_decode_attn_workspace_bytes(ctypes.byref(scheme), batch, n_q_heads, n_kv_heads, max_ctx)
+
+
+def tq_decode_attn_quant(scheme, q, batch, n_q_heads, n_kv_heads, cache, seq_stride_rows,
+                         head_stride_rows, ctx_lens, max_ctx, softmax_scale, signs, out,
+                         workspace, workspace_bytes, stream=None) -> int:
+    return lib().tq_decode_attn_quant(
+        ctypes.byref(scheme), _ptr(q), batch, n_q_heads, n_kv_heads, ctypes.byref(cache),
+        seq_stride_rows, head_stride_rows, _ptr(ctx_lens), max_ctx, softmax_scale, _ptr(signs),
+        _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+# ------------------------------------------------------- torch conveniences
+def scheme(head_dim: int, k_bits: int, v_bits: int) -> Scheme:
+    return Scheme(head_dim, k_bits, v_bits)
+
+
+def rows(n_seq, n_tok, n_head, seq_stride, tok_stride, head_stride) -> Rows:
+    return Rows(n_seq, n_tok, n_head, seq_stride, tok_stride, head_stride)
+
+
+def contiguous_rows(shape) -> Rows:
+    """Rows of a contiguous [L, T, H, ...] tensor."""
+    L, T, H = shape[:3]
+    return Rows(L, T, H, T * H, H, 1)
+
+
+def alloc_planes(sch: Scheme, lead_shape, device) -> dict:
+    """Empty planes of shape lead_shape + [row bytes] (fp16 planes as float16)."""
+    out = {}
+    for i, name in enumerate(PLANES):
+        nbytes = tq_plane_row_bytes(sch, i)
+        if nbytes < 0:
+            raise TQError(nbytes, "tq_plane_row_bytes")
+        if name in ("k_q", "v_q"):
+            out[name] = torch.empty(tuple(lead_shape) + (nbytes,), dtype=torch.uint8, device=device)
+        else:
+            out[name] = torch.empty(tuple(lead_shape) + (nbytes // 2,), dtype=torch.float16, device=device)
+    return out
+
+
+def planes_struct(planes: dict) -> Planes:
+    return Planes(*[planes[n].data_ptr() for n in PLANES])
+
+
+def quantize_kv(k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor, k_bits: int, v_bits: int,
+                out: dict | None = None) -> dict:
+    """Quantize contiguous bf16 [L, T, H, d] K and V into planes [L, T, H, bytes]."""
+    assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and k.shape == v.shape
+    assert k.is_contiguous() and v.is_contiguous() and k.dim() == 4
+    sch = scheme(k.shape[-1], k_bits, v_bits)
+    if out is None:
+        out = alloc_planes(sch, k.shape[:3], k.device)
+    r = contiguous_rows(k.shape)
+    _check(tq_quantize_kv(sch, k, v, r, signs, planes_struct(out), r), "tq_quantize_kv")
+    return out
+
+
+def dequantize_kv(planes: dict, signs: torch.Tensor, head_dim: int, k_bits: int, v_bits: int,
+                  k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None,
+                  keys: bool = True, values: bool = True):
+    """bf16 [L, T, H, d] K and V from contiguous planes [L, T, H, bytes]."""
+    sch = scheme(head_dim, k_bits, v_bits)
+    lead = planes["k_q"].shape[:3]
+    dev = planes["k_q"].device
+    if keys and k_out is None:
+        k_out = torch.empty(tuple(lead) + (head_dim,), dtype=torch.bfloat16, device=dev)
+    if values and v_out is None:
+        v_out = torch.empty(tuple(lead) + (head_dim,), dtype=torch.bfloat16, device=dev)
+    r = contiguous_rows(tuple(lead))
+    _check(tq_dequantize_kv(sch, planes_struct(planes), r, signs, k_out if keys else None,
+                            v_out if values else None, r), "tq_dequantize_kv")
+    return (k_out if keys else None), (v_out if values else None)
+
+
+def quantize_into_cache(k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor, k_bits: int,
+                        v_bits: int, cache: dict | None = None) -> dict:
+    """Quantize bf16 [B, N, Hkv, d] K and V into a cache laid out [B, Hkv, N, bytes]."""
+    B, N, H, d = k.shape
+    sch = scheme(d, k_bits, v_bits)
+    if cache is None:
+        cache = alloc_planes(sch, (B, H, N), k.device)
+    rin = Rows(B, N, H, N * H, H, 1)
+    rout = Rows(B, N, H, H * N, 1, N)
+    _check(tq_quantize_kv(sch, k, v, rin, signs, planes_struct(cache), rout), "tq_quantize_kv")
+    return cache
+
+
+def decode_attn(q: torch.Tensor, cache: dict, ctx_lens: torch.Tensor, signs: torch.Tensor,
+                k_bits: int, v_bits: int, n_kv_heads: int, softmax_scale: float | None = None,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused decode attention; q [B, Hq, d] bf16, cache planes [B, Hkv, N, bytes]."""
+    B, Hq, d = q.shape
+    N = cache["k_q"].shape[2]
+    sch = scheme(d, k_bits, v_bits)
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    ws = tq_decode_attn_workspace_bytes(sch, B, Hq, n_kv_heads, N)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    _check(tq_decode_attn_quant(sch, q, B, Hq, n_kv_heads, planes_struct(cache), n_kv_heads * N, N,
+                                ctx_lens, N, float(softmax_scale), signs, out, workspace,
+                                workspace.numel()), "tq_decode_attn_quant")
+    return out

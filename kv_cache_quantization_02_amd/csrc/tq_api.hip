@@ -1,0 +1,255 @@
+// tq_api.hip -- the C ABI declared in include/tq.h: host-side validation,
+// row-index set-up and kernel dispatch.  Nothing here allocates.
+#include <string.h>
+
+#include "../../include/tq.h"
+#include "tq_codebooks.h"
+#include "tq_launch.h"
+
+namespace {
+
+const uint32_t kCen1[] = {TQ_CENTROIDS_1BIT}, kBnd1[] = {TQ_BOUNDARIES_1BIT};
+const uint32_t kCen2[] = {TQ_CENTROIDS_2BIT}, kBnd2[] = {TQ_BOUNDARIES_2BIT};
+const uint32_t kCen3[] = {TQ_CENTROIDS_3BIT}, kBnd3[] = {TQ_BOUNDARIES_3BIT};
+const uint32_t kCen4[] = {TQ_CENTROIDS_4BIT}, kBnd4[] = {TQ_BOUNDARIES_4BIT};
+const uint32_t kCen5[] = {TQ_CENTROIDS_5BIT}, kBnd5[] = {TQ_BOUNDARIES_5BIT};
+const uint32_t kCen8[] = {TQ_CENTROIDS_8BIT}, kBnd8[] = {TQ_BOUNDARIES_8BIT};
+
+// Cap on the blocks of each half (keys / values) of a codec launch: 8192
+// four-wave blocks per half keep every one of the 256 CUs loaded while the
+// hardware balances the remainder dynamically.
+constexpr int kMaxCodecBlocks = 8192;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int32_t check_scheme(const tq_scheme* s) {
+  if (!s) return TQ_E_NULL;
+  const int d = s->head_dim;
+  if (d != 64 && d != 128 && d != 256 && d != 512) return TQ_E_HEAD_DIM;
+  const int k = s->k_bits, v = s->v_bits;
+  if (k != 2 && k != 4 && k != 5 && k != 8) return TQ_E_BITS;
+  if (v != 2 && v != 3 && v != 4 && v != 5 && v != 8) return TQ_E_BITS;
+  return TQ_OK;
+}
+
+tq::FastDiv make_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const unsigned __int128 num = (unsigned __int128)1 << (31 + l);
+  const uint64_t m = (uint64_t)((num + d - 1) / d);
+  return tq::FastDiv{(uint32_t)m, 31 + l, d};
+}
+
+// Validates a row block; on success fills the row count and index split.
+int32_t check_rows(const tq_rows* r, uint32_t* rows, tq::RowSplit* split) {
+  if (!r) return TQ_E_NULL;
+  if (r->n_seq < 0 || r->n_tok < 0 || r->n_head < 0) return TQ_E_SHAPE;
+  if (r->seq_stride < 0 || r->tok_stride < 0 || r->head_stride < 0) return TQ_E_SHAPE;
+  const unsigned __int128 n = (unsigned __int128)r->n_seq * r->n_tok * r->n_head;
+  if (n >= ((unsigned __int128)1 << 31)) return TQ_E_SHAPE;
+  *rows = (uint32_t)n;
+  if (n) {
+    split->div_head = make_div((uint32_t)r->n_head);
+    split->div_tok = make_div((uint32_t)r->n_tok);
+  }
+  return TQ_OK;
+}
+
+bool same_counts(const tq_rows* a, const tq_rows* b) {
+  return a->n_seq == b->n_seq && a->n_tok == b->n_tok && a->n_head == b->n_head;
+}
+
+tq::RowMap map_of(const tq_rows* r) { return tq::RowMap{r->seq_stride, r->tok_stride, r->head_stride}; }
+
+int32_t check_planes(const tq_planes* p) {
+  if (!p) return TQ_E_NULL;
+  if (!p->k_q || !p->k_scale || !p->k_zero || !p->v_q || !p->v_scale) return TQ_E_NULL;
+  // packed planes are read and written in naturally aligned words of up to
+  // 8 bytes, the fp16 planes in 2-byte words (every plane row length is a
+  // multiple of these, so any row offset keeps the alignment)
+  if (!aligned(p->k_q, 8) || !aligned(p->v_q, 8) || !aligned(p->k_scale, 2) || !aligned(p->k_zero, 2) ||
+      !aligned(p->v_scale, 2))
+    return TQ_E_ALIGN;
+  return TQ_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t tq_check_scheme(const tq_scheme* scheme) { return check_scheme(scheme); }
+
+int64_t tq_plane_row_bytes(const tq_scheme* s, int32_t plane) {
+  const int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  const int64_t d = s->head_dim, g = d / 32;
+  switch (plane) {
+    case TQ_PLANE_K_Q: return d * s->k_bits / 8;
+    case TQ_PLANE_K_SCALE:
+    case TQ_PLANE_K_ZERO:
+    case TQ_PLANE_V_SCALE: return 2 * g;
+    case TQ_PLANE_V_Q: return d * s->v_bits / 8;
+    default: return TQ_E_PLANE;
+  }
+}
+
+int64_t tq_row_bytes(const tq_scheme* s) {
+  const int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  int64_t total = 0;
+  for (int p = 0; p < 5; ++p) total += tq_plane_row_bytes(s, p);
+  return total;
+}
+
+int32_t tq_codebook(int32_t bits, float* centroids, float* boundaries) {
+  const uint32_t *c = nullptr, *b = nullptr;
+  switch (bits) {
+    case 1: c = kCen1; b = kBnd1; break;
+    case 2: c = kCen2; b = kBnd2; break;
+    case 3: c = kCen3; b = kBnd3; break;
+    case 4: c = kCen4; b = kBnd4; break;
+    case 5: c = kCen5; b = kBnd5; break;
+    case 8: c = kCen8; b = kBnd8; break;
+    default: return TQ_E_BITS;
+  }
+  if (!centroids || !boundaries) return TQ_E_NULL;
+  memcpy(centroids, c, sizeof(float) << bits);
+  memcpy(boundaries, b, sizeof(float) * ((1u << bits) - 1));
+  return TQ_OK;
+}
+
+int32_t tq_quantize_kv(const tq_scheme* s, const uint16_t* k_bf16, const uint16_t* v_bf16,
+                       const tq_rows* in_rows, const int8_t* signs, const tq_planes* out,
+                       const tq_rows* out_rows, void* stream) {
+  int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  if (!k_bf16 || !v_bf16 || !signs) return TQ_E_NULL;
+  if ((st = check_planes(out)) != TQ_OK) return st;
+  if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(signs)) return TQ_E_ALIGN;
+  tq::QuantArgs a{};
+  tq::RowSplit split{};
+  uint32_t rows = 0, rows_out = 0;
+  if ((st = check_rows(in_rows, &rows, &split)) != TQ_OK) return st;
+  if ((st = check_rows(out_rows, &rows_out, &split)) != TQ_OK) return st;
+  if (!same_counts(in_rows, out_rows)) return TQ_E_SHAPE;
+  if (rows == 0) return TQ_OK;
+  a.k = k_bf16;
+  a.v = v_bf16;
+  a.signs = signs;
+  a.k_q = (uint8_t*)out->k_q;
+  a.k_scale = (uint16_t*)out->k_scale;
+  a.k_zero = (uint16_t*)out->k_zero;
+  a.v_q = (uint8_t*)out->v_q;
+  a.v_scale = (uint16_t*)out->v_scale;
+  a.rows = rows;
+  a.split = split;
+  a.in = map_of(in_rows);
+  a.out = map_of(out_rows);
+  return hip_status(tq::launch_quantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
+                                        kMaxCodecBlocks));
+}
+
+int32_t tq_dequantize_kv(const tq_scheme* s, const tq_planes* in, const tq_rows* in_rows,
+                         const int8_t* signs, uint16_t* k_bf16, uint16_t* v_bf16,
+                         const tq_rows* out_rows, void* stream) {
+  int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  if ((st = check_planes(in)) != TQ_OK) return st;
+  if (!k_bf16 && !v_bf16) return TQ_E_NULL;
+  if (v_bf16 && !signs) return TQ_E_NULL;
+  if ((k_bf16 && !aligned16(k_bf16)) || (v_bf16 && !aligned16(v_bf16)) || (signs && !aligned16(signs)))
+    return TQ_E_ALIGN;
+  tq::DequantArgs a{};
+  tq::RowSplit split{};
+  uint32_t rows = 0, rows_out = 0;
+  if ((st = check_rows(in_rows, &rows, &split)) != TQ_OK) return st;
+  if ((st = check_rows(out_rows, &rows_out, &split)) != TQ_OK) return st;
+  if (!same_counts(in_rows, out_rows)) return TQ_E_SHAPE;
+  if (rows == 0) return TQ_OK;
+  a.k_q = (const uint8_t*)in->k_q;
+  a.k_scale = (const uint16_t*)in->k_scale;
+  a.k_zero = (const uint16_t*)in->k_zero;
+  a.v_q = (const uint8_t*)in->v_q;
+  a.v_scale = (const uint16_t*)in->v_scale;
+  a.signs = signs;
+  a.k = k_bf16;
+  a.v = v_bf16;
+  a.rows = rows;
+  a.split = split;
+  a.in = map_of(in_rows);
+  a.out = map_of(out_rows);
+  return hip_status(tq::launch_dequantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
+                                          kMaxCodecBlocks));
+}
+
+size_t tq_decode_attn_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t max_ctx) {
+  if (check_scheme(s) != TQ_OK) return 0;
+  if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1) return 0;
+  int splits = 0, tps = 0;
+  tq::decode_attn_geometry(s->head_dim, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
+  return tq::decode_attn_part_bytes(s->head_dim, batch, n_q_heads, splits);
+}
+
+int32_t tq_decode_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache,
+                             int64_t seq_stride_rows, int64_t head_stride_rows,
+                             const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
+                             const int8_t* signs, uint16_t* out_bf16, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1 ||
+      seq_stride_rows < 0 || head_stride_rows < 0)
+    return TQ_E_SHAPE;
+  if (batch == 0) return TQ_OK;
+  if (!q_bf16 || !ctx_lens || !signs || !out_bf16) return TQ_E_NULL;
+  if ((st = check_planes(cache)) != TQ_OK) return st;
+  if (!aligned16(q_bf16) || !aligned16(signs) || !aligned16(out_bf16)) return TQ_E_ALIGN;
+  int splits = 0, tps = 0;
+  tq::decode_attn_geometry(s->head_dim, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
+  if (!workspace || workspace_bytes < tq::decode_attn_part_bytes(s->head_dim, batch, n_q_heads, splits))
+    return TQ_E_WORKSPACE;
+  if (!aligned16(workspace)) return TQ_E_ALIGN;
+  tq::AttnArgs a{};
+  a.q = q_bf16;
+  a.k_q = (const uint8_t*)cache->k_q;
+  a.k_scale = (const uint16_t*)cache->k_scale;
+  a.k_zero = (const uint16_t*)cache->k_zero;
+  a.v_q = (const uint8_t*)cache->v_q;
+  a.v_scale = (const uint16_t*)cache->v_scale;
+  a.signs = signs;
+  a.ctx_lens = ctx_lens;
+  a.out = out_bf16;
+  a.part = (float*)workspace;
+  a.seq_stride = seq_stride_rows;
+  a.head_stride = head_stride_rows;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.max_ctx = max_ctx;
+  a.splits = splits;
+  a.tokens_per_split = tps;
+  a.softmax_scale = softmax_scale;
+  return hip_status(tq::launch_decode_attn(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream));
+}
+
+const char* tq_status_string(int32_t status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_E_HEAD_DIM: return "head_dim must be 64, 128, 256 or 512";
+    case TQ_E_BITS: return "k_bits must be 2, 4, 5 or 8 and v_bits 2, 3, 4, 5 or 8";
+    case TQ_E_NULL: return "a required pointer is null";
+    case TQ_E_SHAPE: return "invalid counts or strides";
+    case TQ_E_ALIGN: return "a base pointer is not suitably aligned";
+    case TQ_E_WORKSPACE: return "decode workspace missing or too small";
+    case TQ_E_HIP: return "HIP launch error";
+    case TQ_E_PLANE: return "plane index out of range";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

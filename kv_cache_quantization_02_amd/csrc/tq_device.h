@@ -1,0 +1,165 @@
+// tq_device.h -- gfx950 device helpers shared by the codec and attention kernels.
+//
+// Lane layout used by every codec kernel: a (token, kv-head) row of d
+// elements is spread over d/8 consecutive lanes of a wave64, lane `sub` of
+// the row holding elements 8*sub .. 8*sub+7 (one 16-byte bf16 load).  A
+// 32-element group therefore lives in 4 consecutive lanes, and the
+// Walsh-Hadamard stages h = 1, 2, 4 run inside a lane while h = 8 << k pairs
+// lanes sub and sub ^ (1 << k).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kGroup = 32;
+
+struct RowMap {
+  int64_t seq_stride, tok_stride, head_stride;
+};
+
+// Exact unsigned division n / d for n < 2^31 by a multiply and a shift
+// (Granlund & Montgomery 1994, Thm 4.2 with N = 31): m = ceil(2^(31+l) / d),
+// l = ceil(log2 d), q = (m * n) >> (31 + l).
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shift;  // 31 + l
+  uint32_t d;
+};
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)f.mul * n) >> f.shift);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// bf16 pair (round to nearest even by the hardware converter).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// fp16 pattern of a float, round to nearest even; every NaN -> 0x7E00.
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  _Float16 h = (_Float16)x;
+  uint32_t b = __builtin_bit_cast(uint16_t, h);
+  return (x != x) ? 0x7E00u : b;
+}
+
+__device__ __forceinline__ float f16_value(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Replace any NaN by the default quiet NaN so that every NaN an output
+// inherits from it rounds to the canonical bf16 NaN.
+__device__ __forceinline__ float canon_nan(float x) {
+  return (x != x) ? __uint_as_float(0x7FC00000u) : x;
+}
+
+// The value `x` held by lane (lane ^ M), for M a power of two below 64.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  int v = __float_as_int(x);
+  if constexpr (M == 1) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 8) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, true);  // row_ror:8
+  } else if constexpr (M == 4 || M == 16) {
+    v = __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1F);  // bit mode, xor M
+  } else {
+    static_assert(M == 32, "lane_xor: unsupported mask");
+    v = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), v);
+  }
+  return __int_as_float(v);
+}
+
+// Walsh-Hadamard stages h = 1, 2, 4 on the 8 elements held by this lane:
+// (u_i, u_{i+h}) <- (u_i + u_{i+h}, u_i - u_{i+h}).
+__device__ __forceinline__ void fwht_in_lane(float (&y)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i & h) == 0) {
+        const float a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Stage h = 8*M across lanes: the lane with bit M clear holds u_i and forms
+// u_i + u_{i+h}; its partner holds u_{i+h} and forms u_i - u_{i+h}.  Both are
+// one rounding of sgn*self + partner with sgn = +1 / -1 (fma is exact here).
+template <int M>
+__device__ __forceinline__ void fwht_cross(float (&y)[8], float sgn) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = __builtin_fmaf(sgn, y[i], lane_xor<M>(y[i]));
+}
+
+// All stages h = 1 .. D/2 in ascending order, for the layout above.
+template <int D>
+__device__ __forceinline__ void fwht_row(float (&y)[8], int sub) {
+  fwht_in_lane(y);
+  if constexpr (D >= 16) fwht_cross<1>(y, (sub & 1) ? -1.f : 1.f);
+  if constexpr (D >= 32) fwht_cross<2>(y, (sub & 2) ? -1.f : 1.f);
+  if constexpr (D >= 64) fwht_cross<4>(y, (sub & 4) ? -1.f : 1.f);
+  if constexpr (D >= 128) fwht_cross<8>(y, (sub & 8) ? -1.f : 1.f);
+  if constexpr (D >= 256) fwht_cross<16>(y, (sub & 16) ? -1.f : 1.f);
+  if constexpr (D >= 512) fwht_cross<32>(y, (sub & 32) ? -1.f : 1.f);
+}
+
+// Float32 1/sqrt(d) for the supported head dims.
+template <int D>
+__device__ __forceinline__ float inv_sqrt_d() {
+  if constexpr (D == 64) return __uint_as_float(0x3E000000u);
+  else if constexpr (D == 128) return __uint_as_float(0x3DB504F3u);
+  else if constexpr (D == 256) return __uint_as_float(0x3D800000u);
+  else return __uint_as_float(0x3D3504F3u);
+}
+
+// The B*8 bits of this lane's 8 packed elements (stream bytes B*sub ..
+// B*sub+B-1 of the row), loaded with naturally aligned accesses that never
+// leave the row (row lengths are multiples of 8 bytes).
+template <int B>
+__device__ __forceinline__ uint64_t load_lane_bits(const uint8_t* row, int sub) {
+  if constexpr (B == 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + 8 * sub);
+    return (uint64_t)w.x | ((uint64_t)w.y << 32);
+  } else if constexpr (B == 4) {
+    return *reinterpret_cast<const uint32_t*>(row + 4 * sub);
+  } else if constexpr (B == 2) {
+    return *reinterpret_cast<const uint16_t*>(row + 2 * sub);
+  } else {
+    const int off = B * sub;
+    const int a = off & ~3;
+    const int sh = (off & 3) * 8;
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(row + a);
+    uint32_t w1 = 0;
+    if ((off & 3) + B > 4) w1 = *reinterpret_cast<const uint32_t*>(row + a + 4);
+    return (((uint64_t)w1 << 32) | w0) >> sh;
+  }
+}
+
+// Store the low B bytes of `bits` at stream bytes B*sub .. of the row.
+template <int B>
+__device__ __forceinline__ void store_lane_bits(uint8_t* row, int sub, uint64_t bits) {
+  if constexpr (B == 8) {
+    *reinterpret_cast<uint2*>(row + 8 * sub) = make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
+  } else if constexpr (B == 4) {
+    *reinterpret_cast<uint32_t*>(row + 4 * sub) = (uint32_t)bits;
+  } else if constexpr (B == 2) {
+    *reinterpret_cast<uint16_t*>(row + 2 * sub) = (uint16_t)bits;
+  } else {
+#pragma unroll
+    for (int i = 0; i < B; ++i) row[B * sub + i] = (uint8_t)(bits >> (8 * i));
+  }
+}
+
+}  // namespace tq

@@ -1,0 +1,71 @@
+// tq_launch.h -- argument blocks passed by value to the kernels, and the
+// host-side launchers each kernel file exports to the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_device.h"
+
+namespace tq {
+
+// Row r in [0, rows) is (s, t, h) with r = (s * n_tok + t) * n_head + h.
+struct RowSplit {
+  FastDiv div_head;  // divides by n_head
+  FastDiv div_tok;   // divides by n_tok
+};
+
+struct QuantArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int8_t* signs;
+  uint8_t* k_q;
+  uint16_t* k_scale;
+  uint16_t* k_zero;
+  uint8_t* v_q;
+  uint16_t* v_scale;
+  uint32_t rows;
+  RowSplit split;
+  RowMap in, out;
+};
+
+struct DequantArgs {
+  const uint8_t* k_q;
+  const uint16_t* k_scale;
+  const uint16_t* k_zero;
+  const uint8_t* v_q;
+  const uint16_t* v_scale;
+  const int8_t* signs;
+  uint16_t* k;  // may be null: keys skipped
+  uint16_t* v;  // may be null: values skipped
+  uint32_t rows;
+  RowSplit split;
+  RowMap in, out;
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint8_t* k_q;
+  const uint16_t* k_scale;
+  const uint16_t* k_zero;
+  const uint8_t* v_q;
+  const uint16_t* v_scale;
+  const int8_t* signs;
+  const int32_t* ctx_lens;
+  uint16_t* out;
+  float* part;  // [batch, n_q_heads, splits, head_dim + 4]: acc[d], m, l, pad
+  int64_t seq_stride, head_stride;
+  int32_t batch, n_q_heads, n_kv_heads, max_ctx, splits, tokens_per_split;
+  float softmax_scale;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
+hipError_t launch_dequantize(const DequantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
+hipError_t launch_decode_attn(const AttnArgs& a, int d, int kb, int vb, hipStream_t st);
+
+// Split-K decode geometry for a given problem (shared by the workspace query).
+void decode_attn_geometry(int d, int batch, int n_q_heads, int n_kv_heads, int max_ctx, int* splits,
+                          int* tokens_per_split);
+size_t decode_attn_part_bytes(int d, int batch, int n_q_heads, int splits);
+
+}  // namespace tq
