@@ -86,7 +86,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=262144)
+    ap.add_argument("--cpu-rows", type=int, default=1048576)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run plain 1 GiB device copies (untimed) so a "
+                         "counter run can scale FETCH_SIZE/WRITE_SIZE by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the codec shards by layer or kv-head with no "
@@ -178,6 +181,14 @@ def main():
     roofline = {"bound": "hbm", "achieved": phases[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": phases[dom]["GBps"] / HBM_PEAK_GBS, "traffic": measured_traffic(kname),
                 "kernel": phases[dom]["kernel"], "algorithmic_bytes_per_launch": dom_bytes}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
