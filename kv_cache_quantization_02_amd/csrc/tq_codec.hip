@@ -4,13 +4,38 @@
 //   keys   : asymmetric affine per 32-group, fp32 arithmetic, fp16 scale/zero;
 //   values : y = FWHT(x * signs) / sqrt(d); RMS per 32-group; Lloyd-Max index
 //            of y / (scale + 1e-8); little-endian packed bitstream.
-// Every kernel streams rows with the layout described in tq_device.h and a
-// grid-stride loop over rows; a wave handles 64*8/d rows per iteration.
+//
+// These kernels are bound by VALU issue, not by HBM, so the layout is chosen
+// to minimise vector instructions per row:
+//   * one lane owns one whole 32-element group (64 contiguous bf16 bytes), so
+//     group min/max, the mean square and every per-group scalar (divisions,
+//     square root, fp16 conversion) are computed once, inside the lane;
+//   * the row's groups sit on lanes whose xor partners are DPP-reachable
+//     (g bit 0 -> lane xor 1, bit 1 -> xor 2, bit 2 -> xor 8, bit 3 -> xor 4),
+//     so each cross-lane transform stage is one v_fmac_f32_dpp per element;
+//   * divisions by the group scale are exact via one correctly rounded
+//     reciprocal and Markstein's correction, 3 operations per element.
+// Quantize and dequantize are one launch each: even blocks stream key rows,
+// odd blocks value rows.
 #include "tq_codebooks.h"
 #include "tq_device.h"
 #include "tq_launch.h"
 
+#include <utility>
+
 namespace tq {
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 with I a
+// compile-time constant, so per-batch arrays are indexed statically and stay
+// in registers (a runtime loop index would move them to scratch memory).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __constant__ uint32_t c_bnd_2[3] = {TQ_BOUNDARIES_2BIT};
 __constant__ uint32_t c_bnd_3[7] = {TQ_BOUNDARIES_3BIT};
@@ -41,6 +66,94 @@ __device__ __forceinline__ const uint32_t* centroids() {
   else return c_cen_8;
 }
 
+// ------------------------------------------------------------ lane layout
+// D/32 lanes per row, 64/(D/32) rows per wave; lane -> (group g, row rw).
+template <int D>
+struct GroupLanes {
+  static constexpr int LPR = D / kGroup;
+  static constexpr int RPW = 64 / LPR;
+  static constexpr int NSTAGE = (D == 64) ? 1 : (D == 128) ? 2 : (D == 256) ? 3 : 4;
+  __device__ static int group(int lane) {
+    if constexpr (D == 64) return lane & 1;
+    else if constexpr (D == 128) return lane & 3;
+    else if constexpr (D == 256) return (lane & 3) | (((lane >> 3) & 1) << 2);
+    else return (lane & 3) | (((lane >> 3) & 1) << 2) | (((lane >> 2) & 1) << 3);
+  }
+  __device__ static int row(int lane) {
+    if constexpr (D == 64) return lane >> 1;
+    else if constexpr (D == 128) return lane >> 2;
+    else if constexpr (D == 256) return ((lane >> 2) & 1) | ((lane >> 4) << 1);
+    else return lane >> 4;
+  }
+};
+
+// The lane mask that pairs groups g and g ^ (1 << k).
+template <int K>
+constexpr int stage_mask() { return K == 0 ? 1 : K == 1 ? 2 : K == 2 ? 8 : 4; }
+
+// w += c * w(lane ^ M) for all 32 elements: one DPP-fused fmac per element
+// for M in {1, 2, 8}; a swizzle plus an fma for M = 4.
+template <int M>
+__device__ __forceinline__ void cross_stage(float (&w)[32], float c) {
+  if constexpr (M == 4) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = __builtin_fmaf(lane_xor<4>(w[i]), c, w[i]);
+  } else {
+#define TQ_FMAC_DPP8(CTRL)                                                                      \
+  asm volatile("s_nop 1\n\t"                                                                    \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL "\n\t"                                        \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL "\n\t"                                        \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL "\n\t"                                        \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL "\n\t"                                        \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL "\n\t"                                        \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL "\n\t"                                        \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL "\n\t"                                        \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL                                               \
+               : "+v"(w[j]), "+v"(w[j + 1]), "+v"(w[j + 2]), "+v"(w[j + 3]), "+v"(w[j + 4]),   \
+                 "+v"(w[j + 5]), "+v"(w[j + 6]), "+v"(w[j + 7])                                \
+               : "v"(c))
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+      if constexpr (M == 1)
+        TQ_FMAC_DPP8("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1");
+      else if constexpr (M == 2)
+        TQ_FMAC_DPP8("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1");
+      else
+        TQ_FMAC_DPP8("row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1");
+    }
+#undef TQ_FMAC_DPP8
+  }
+}
+
+// Unnormalised Walsh-Hadamard transform of the row, stages h = 1 .. D/2 in
+// ascending order.  Stages below 32 run inside the lane; stage h = 32 * 2^k
+// pairs this lane with lane ^ stage_mask<k>.  The lane holding the upper
+// element of a cross pair computes self - partner, the negative of the true
+// value, so the result is sigma * FWHT with sigma = +-1 per lane; the sign is
+// returned so the caller folds it into its final multiply.
+template <int D>
+__device__ __forceinline__ float fwht_group(float (&w)[32], int lane) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = w[i], b = w[i + h];
+        w[i] = a + b;
+        w[i + h] = a - b;
+      }
+    }
+  }
+  float sigma = 1.f;
+  constexpr int NS = GroupLanes<D>::NSTAGE;
+  if constexpr (NS >= 1) { const float c = (lane & stage_mask<0>()) ? -1.f : 1.f; cross_stage<stage_mask<0>()>(w, c); sigma *= c; }
+  if constexpr (NS >= 2) { const float c = (lane & stage_mask<1>()) ? -1.f : 1.f; cross_stage<stage_mask<1>()>(w, c); sigma *= c; }
+  if constexpr (NS >= 3) { const float c = (lane & stage_mask<2>()) ? -1.f : 1.f; cross_stage<stage_mask<2>()>(w, c); sigma *= c; }
+  if constexpr (NS >= 4) { const float c = (lane & stage_mask<3>()) ? -1.f : 1.f; cross_stage<stage_mask<3>()>(w, c); sigma *= c; }
+  return sigma;
+}
+
+// ------------------------------------------------------------ row helpers
 __device__ __forceinline__ void split_row(uint32_t r, const RowSplit& rs, uint32_t& s, uint32_t& t,
                                           uint32_t& h) {
   const uint32_t st = fast_div(r, rs.div_head);
@@ -53,38 +166,55 @@ __device__ __forceinline__ int64_t row_index(const RowMap& m, uint32_t s, uint32
   return (int64_t)s * m.seq_stride + (int64_t)t * m.tok_stride + (int64_t)h * m.head_stride;
 }
 
-__device__ __forceinline__ void unpack8(const uint4 w, float (&x)[8]) {
-  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
-  x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
-  x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-}
-
-__device__ __forceinline__ void lane_signs(const int8_t* signs, int sub, float (&sg)[8]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(signs + 8 * sub);
+// 32 bf16 (64 bytes) -> 16 raw words.
+__device__ __forceinline__ void load_group(const uint16_t* p, uint32_t (&u)[16]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t word = i < 4 ? w.x : w.y;
-    const int8_t b = (int8_t)(word >> (8 * (i & 3)));
-    sg[i] = b < 0 ? -1.f : 1.f;
+  for (int j = 0; j < 4; ++j) {
+    const uint4 v = q[j];
+    u[4 * j] = v.x; u[4 * j + 1] = v.y; u[4 * j + 2] = v.z; u[4 * j + 3] = v.w;
   }
 }
 
-// Count of ascending boundaries strictly below y (searchsorted, left side);
-// NaN compares false everywhere and gives 0.
+// Exact division of every element by a per-group divisor s: with r = RN(1/s),
+// q0 = RN(y r), e = y - q0 s (exact by fma), q = RN(q0 + e r) equals RN(y/s)
+// (Markstein 1990) while s is a normal number and no step overflows.
+__device__ __forceinline__ float div_markstein(float y, float s, float r) {
+  const float q0 = y * r;
+  const float e = __builtin_fmaf(-q0, s, y);
+  return __builtin_fmaf(e, r, q0);
+}
+
+__device__ __forceinline__ bool normal_divisor(float s) {
+  // 2^-100 <= |s| < 2^100 keeps every Markstein step away from the
+  // subnormal and overflow ranges; other divisors take the exact '/'.
+  const float a = __builtin_fabsf(s);
+  return a >= 7.88860905e-31f && a < 1.26765060e+30f;
+}
+
+// Lloyd-Max index #{boundaries < yn}, yn = RN(y / den) exact.  Odd widths
+// with symmetric tables are searched on the magnitude: key = bits(yn)
+// rotated left by one (the sign lands in bit 0), so for a non-negative
+// boundary b with key-threshold 2*bits(b), key > 2*bits(b) holds exactly when
+// b < yn for yn >= 0 and when b <= |yn| for yn < 0 -- the two cases the count
+// needs -- and the index is then c ^ (yn > 0 ? H+1 : H) with H the number of
+// negative boundaries.  NaN yn gives 0.
 template <int B>
-__device__ __forceinline__ uint32_t lloyd_max_index(float y, const float* lds_bnd) {
-  if constexpr (B <= 3) {
+__device__ __forceinline__ uint32_t lloyd_max_index(float yn, const float* lds_bnd) {
+  if constexpr (B <= 4) {
+    constexpr int H = (1 << (B - 1)) - 1;  // negative boundaries; boundary H is 0
     const uint32_t* bnd = boundaries<B>();
-    uint32_t idx = 0;
+    const uint32_t key = __builtin_amdgcn_alignbit(__float_as_uint(yn), __float_as_uint(yn), 31);
+    uint32_t c = 0;
 #pragma unroll
-    for (int k = 0; k < (1 << B) - 1; ++k) idx += (__uint_as_float(bnd[k]) < y) ? 1u : 0u;
-    return idx;
+    for (int j = 1; j <= H; ++j) c += (key > (bnd[H + j] << 1)) ? 1u : 0u;
+    const uint32_t base = (yn > 0.f) ? (uint32_t)(H + 1) : (uint32_t)H;
+    return c ^ base;
   } else {
     uint32_t idx = 0;
 #pragma unroll
     for (int step = 1 << (B - 1); step >= 1; step >>= 1)
-      idx += (lds_bnd[idx + step - 1] < y) ? (uint32_t)step : 0u;
+      idx += (lds_bnd[idx + step - 1] < yn) ? (uint32_t)step : 0u;
     return idx;
   }
 }
@@ -92,32 +222,33 @@ __device__ __forceinline__ uint32_t lloyd_max_index(float y, const float* lds_bn
 // ------------------------------------------------------------------ keys
 template <int D, int KB>
 __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t blk, uint32_t nblk) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR, G = D / kGroup;
-  const int lane = threadIdx.x & 63, sub = lane % LPR, rw = lane / LPR;
+  using L = GroupLanes<D>;
+  constexpr int G = D / kGroup;
+  const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
   const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
   const uint32_t nwave = nblk * 4u;
   const float lo = KB == 8 ? -127.f : 0.f;
   const float hi = KB == 8 ? 127.f : (float)((1 << KB) - 1);
-  for (uint32_t base = wave * RPW; base < a.rows; base += nwave * RPW) {
+  for (uint32_t base = wave * L::RPW; base < a.rows; base += nwave * L::RPW) {
     const uint32_t r = base + rw;
-    const bool active = r < a.rows;
+    if (r >= a.rows) continue;
     uint32_t s, t, h;
-    split_row(active ? r : 0u, a.split, s, t, h);
+    split_row(r, a.split, s, t, h);
     const int64_t irow = row_index(a.in, s, t, h), orow = row_index(a.out, s, t, h);
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (active) w = *reinterpret_cast<const uint4*>(a.k + irow * D + 8 * sub);
-    float x[8];
-    unpack8(w, x);
+    uint32_t u[16];
+    load_group(a.k + irow * D + kGroup * g, u);
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[2 * i] = bf16_lo(u[i]);
+      x[2 * i + 1] = bf16_hi(u[i]);
+    }
     float mn = x[0], mx = x[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
+    for (int i = 1; i < 32; ++i) {
       mn = __builtin_elementwise_minimum(mn, x[i]);
       mx = __builtin_elementwise_maximum(mx, x[i]);
     }
-    mn = __builtin_elementwise_minimum(mn, lane_xor<1>(mn));
-    mx = __builtin_elementwise_maximum(mx, lane_xor<1>(mx));
-    mn = __builtin_elementwise_minimum(mn, lane_xor<2>(mn));
-    mx = __builtin_elementwise_maximum(mx, lane_xor<2>(mx));
     float scale, zero;
     if constexpr (KB == 8) {
       scale = (mx - mn) / 254.0f;
@@ -126,154 +257,355 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
       scale = (mx - mn) / (float)((1 << KB) - 1);
       zero = __builtin_rintf(mn / scale);
     }
-    uint64_t bits = 0;
+    const bool fast = normal_divisor(scale);
+    const float rcp = 1.0f / scale;
+    float q[32];
+    if (fast) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float tq = x[i] / scale - zero;
-      const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(tq), lo), hi);
-      if constexpr (KB == 8)
-        bits |= (uint64_t)(uint8_t)(int8_t)(int)q << (8 * i);
-      else
-        bits |= (uint64_t)(uint32_t)(int)q << (KB * i);
+      for (int i = 0; i < 32; ++i) q[i] = div_markstein(x[i], scale, rcp);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) q[i] = x[i] / scale;
     }
-    if (active) {
-      store_lane_bits<KB>(a.k_q + orow * (D * KB / 8), sub, bits);
-      if ((sub & 3) == 0) {
-        a.k_scale[orow * G + (sub >> 2)] = (uint16_t)f16_bits(scale);
-        a.k_zero[orow * G + (sub >> 2)] = (uint16_t)f16_bits(zero);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) q[i] = __builtin_fminf(__builtin_fmaxf(q[i] - zero, lo), hi);
+    if constexpr (KB == 8) {
+      // round half-to-even into the low byte by adding 1.5 * 2^23, then gather
+      // the four low bytes of each quad of floats
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b0 = __float_as_uint(q[4 * i] + 12582912.0f);
+        const uint32_t b1 = __float_as_uint(q[4 * i + 1] + 12582912.0f);
+        const uint32_t b2 = __float_as_uint(q[4 * i + 2] + 12582912.0f);
+        const uint32_t b3 = __float_as_uint(q[4 * i + 3] + 12582912.0f);
+        const uint32_t lo2 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+        const uint32_t hi2 = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
+        o[i] = lo2 | hi2;
       }
+      // the key plane is only 8-byte aligned: four 8-byte stores
+      uint2* dst = reinterpret_cast<uint2*>(a.k_q + orow * D + kGroup * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = make_uint2(o[2 * i], o[2 * i + 1]);
+    } else {
+      uint32_t o[KB] = {};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t v = (uint32_t)__builtin_rintf(q[i]);
+        const int bit = KB * i, wd = bit >> 5, off = bit & 31;
+        o[wd] |= v << off;
+        if (off + KB > 32) o[wd + 1] |= v >> (32 - off);
+      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_q + orow * (D * KB / 8) + 4 * KB * g);
+#pragma unroll
+      for (int i = 0; i < KB; ++i) dst[i] = o[i];
     }
+    a.k_scale[orow * G + g] = (uint16_t)f16_bits(scale);
+    a.k_zero[orow * G + g] = (uint16_t)f16_bits(zero);
   }
 }
 
 // ---------------------------------------------------------------- values
 template <int D, int VB>
 __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_t blk, uint32_t nblk) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR, G = D / kGroup;
-  __shared__ float bnd_lds[VB >= 4 ? (1 << VB) : 1];
-  if constexpr (VB >= 4) {
+  using L = GroupLanes<D>;
+  constexpr int G = D / kGroup;
+  __shared__ float bnd_lds[VB >= 5 ? (1 << VB) : 1];
+  if constexpr (VB >= 5) {
     for (int i = threadIdx.x; i < (1 << VB) - 1; i += blockDim.x)
       bnd_lds[i] = __uint_as_float(boundaries<VB>()[i]);
     __syncthreads();
   }
-  const int lane = threadIdx.x & 63, sub = lane % LPR, rw = lane / LPR;
+  const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
   const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
   const uint32_t nwave = nblk * 4u;
-  float sg[8];
-  lane_signs(a.signs, sub, sg);
+  // sign masks of this lane's 32 elements, two per bf16 pair (bits 15 and 31)
+  uint32_t smask[16];
+  {
+    const uint4* sp = reinterpret_cast<const uint4*>(a.signs + kGroup * g);
+    const uint4 s0 = sp[0], s1 = sp[1];
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t word = sw[i >> 1] >> (16 * (i & 1));
+      smask[i] = ((word & 0x80u) << 8) | ((word & 0x8000u) << 16);
+    }
+  }
   const float rd = inv_sqrt_d<D>();
-  for (uint32_t base = wave * RPW; base < a.rows; base += nwave * RPW) {
+  for (uint32_t base = wave * L::RPW; base < a.rows; base += nwave * L::RPW) {
     const uint32_t r = base + rw;
     const bool active = r < a.rows;
     uint32_t s, t, h;
     split_row(active ? r : 0u, a.split, s, t, h);
     const int64_t irow = row_index(a.in, s, t, h), orow = row_index(a.out, s, t, h);
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (active) w = *reinterpret_cast<const uint4*>(a.v + irow * D + 8 * sub);
-    float y[8];
-    unpack8(w, y);
+    uint32_t u[16];
+    if (active) {
+      load_group(a.v + irow * D + kGroup * g, u);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = y[i] * sg[i];
-    fwht_row<D>(y, sub);
+      for (int i = 0; i < 16; ++i) u[i] = 0;
+    }
+    float w[32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = y[i] * rd;
-    // mean square of the 32-group: adjacent pairs, then pairs of pairs, ...
-    const float e01 = y[0] * y[0] + y[1] * y[1];
-    const float e23 = y[2] * y[2] + y[3] * y[3];
-    const float e45 = y[4] * y[4] + y[5] * y[5];
-    const float e67 = y[6] * y[6] + y[7] * y[7];
-    float e = (e01 + e23) + (e45 + e67);
-    e = e + lane_xor<1>(e);
-    e = e + lane_xor<2>(e);
-    const float scale = __builtin_sqrtf(e * 0.03125f);
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t x = u[i] ^ smask[i];
+      w[2 * i] = bf16_lo(x);
+      w[2 * i + 1] = bf16_hi(x);
+    }
+    const float m = fwht_group<D>(w, lane) * rd;
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = w[i] * m;
+    // mean square: adjacent pairs, then pairs of pairs, ... (fixed tree)
+    float e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = y[2 * i] * y[2 * i] + y[2 * i + 1] * y[2 * i + 1];
+#pragma unroll
+    for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+      for (int i = 0; i < n; ++i) e[i] = e[2 * i] + e[2 * i + 1];
+    const float scale = __builtin_sqrtf(e[0] * 0.03125f);
     const float den = scale + 1e-8f;
-    uint64_t bits = 0;
+    const bool fast = normal_divisor(den);
+    const float rcp = 1.0f / den;
+    if (fast) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t idx = lloyd_max_index<VB>(y[i] / den, bnd_lds);
-      bits |= (uint64_t)idx << (VB * i);
+      for (int i = 0; i < 32; ++i) y[i] = div_markstein(y[i], den, rcp);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) y[i] = y[i] / den;
+    }
+    uint32_t o[VB] = {};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t idx = lloyd_max_index<VB>(y[i], bnd_lds);
+      const int bit = VB * i, wd = bit >> 5, off = bit & 31;
+      o[wd] |= idx << off;
+      if (off + VB > 32) o[wd + 1] |= idx >> (32 - off);
     }
     if (active) {
-      store_lane_bits<VB>(a.v_q + orow * (D * VB / 8), sub, bits);
-      if ((sub & 3) == 0) a.v_scale[orow * G + (sub >> 2)] = (uint16_t)f16_bits(scale);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.v_q + orow * (D * VB / 8) + 4 * VB * g);
+#pragma unroll
+      for (int i = 0; i < VB; ++i) dst[i] = o[i];
+      a.v_scale[orow * G + g] = (uint16_t)f16_bits(scale);
     }
   }
 }
 
 // ------------------------------------------------------------- dequantize
+// Output staging for the dequantize kernels.  A wave's 64 lanes hold
+// 64 x 64 bytes = one 4 KB tile of RPW consecutive bf16 rows (lane (rw, g)
+// holds bytes 64g .. 64g+63 of row rw).  Storing that straight from the
+// group layout writes partial cache lines and costs ~1.6x the bytes at HBM,
+// so the tile goes through LDS (every 64 bytes padded by 16 so the writes are
+// bank-conflict free) and is stored back as chunk c = lane + 64j (j = 0..3)
+// of the row-major tile: each store instruction then covers whole rows.
+// Row offsets travel through LDS too; a negative offset marks a row past the end.
+constexpr int kTileBytes = 64 * 80;  // 64 lanes x (64 + 16 pad) bytes
+
+__device__ __forceinline__ int tile_offset(int chunk) { return 16 * chunk + 16 * (chunk >> 2); }
+
+template <int D>
+__device__ __forceinline__ void store_tile(const uint32_t (&o)[16], uint16_t* base, int64_t my_off,
+                                           uint8_t* tile, int64_t* offs, int lane, int g, int rw) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per bf16 row
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<uint4*>(tile + tile_offset(rw * CPR + 4 * g + j)) =
+        make_uint4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+  if (g == 0) offs[rw] = my_off;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = lane + 64 * j;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_offset(c));
+    const int64_t off = offs[c / CPR];
+    if (off >= 0) *reinterpret_cast<uint4*>(base + off + 8 * (c % CPR)) = v;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Dequantize loops take kBatch rows per lane per pass and issue all their
+// loads before any arithmetic: a lane reads only 12-36 packed bytes per row,
+// so this keeps enough bytes in flight to cover HBM latency.
+constexpr int kBatch = 4;
+
 template <int D, int KB>
 __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint32_t blk, uint32_t nblk) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR, G = D / kGroup;
-  const int lane = threadIdx.x & 63, sub = lane % LPR, rw = lane / LPR;
+  using L = GroupLanes<D>;
+  constexpr int G = D / kGroup;
+  constexpr int KW = KB == 8 ? 8 : KB;  // packed words per lane
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][kTileBytes];
+  __shared__ int64_t row_offs[4][L::RPW];
+  const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
+  uint8_t* tile = tiles[threadIdx.x >> 6];
+  int64_t* offs = row_offs[threadIdx.x >> 6];
   const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
-  const uint32_t nwave = nblk * 4u;
-  for (uint32_t base = wave * RPW; base < a.rows; base += nwave * RPW) {
-    const uint32_t r = base + rw;
-    if (r >= a.rows) continue;
-    uint32_t s, t, h;
-    split_row(r, a.split, s, t, h);
-    const int64_t irow = row_index(a.in, s, t, h), orow = row_index(a.out, s, t, h);
-    const uint64_t bits = load_lane_bits<KB>(a.k_q + irow * (D * KB / 8), sub);
-    const float sc = canon_nan(f16_value(a.k_scale[irow * G + (sub >> 2)]));
-    const float zp = canon_nan(f16_value(a.k_zero[irow * G + (sub >> 2)]));
-    float k[8];
+  const uint32_t step = nblk * 4u * L::RPW;
+  for (uint32_t base = wave * L::RPW; base < a.rows; base += kBatch * step) {
+    uint32_t wv[kBatch][KW];
+    float sc[kBatch], zp[kBatch];
+    int64_t orow[kBatch];
+    bool act[kBatch];
+    static_for<kBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const uint32_t r = base + u * step + rw;
+      act[u] = r < a.rows;
+      uint32_t s, t, h;
+      split_row(act[u] ? r : 0u, a.split, s, t, h);
+      const int64_t irow = row_index(a.in, s, t, h);
+      orow[u] = row_index(a.out, s, t, h);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q;
-      if constexpr (KB == 8)
-        q = (float)(int8_t)(bits >> (8 * i));
-      else
-        q = (float)(uint32_t)((bits >> (KB * i)) & ((1u << KB) - 1));
-      k[i] = (q + zp) * sc;
-    }
-    uint4 o;
-    o.x = pack_bf16x2(k[0], k[1]);
-    o.y = pack_bf16x2(k[2], k[3]);
-    o.z = pack_bf16x2(k[4], k[5]);
-    o.w = pack_bf16x2(k[6], k[7]);
-    *reinterpret_cast<uint4*>(a.k + orow * D + 8 * sub) = o;
+      for (int i = 0; i < KW; ++i) wv[u][i] = 0;
+      if (act[u]) {
+        if constexpr (KB == 8) {
+          const uint2* src = reinterpret_cast<const uint2*>(a.k_q + irow * D + kGroup * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint2 v = src[i];
+            wv[u][2 * i] = v.x;
+            wv[u][2 * i + 1] = v.y;
+          }
+        } else {
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k_q + irow * (D * KB / 8) + 4 * KB * g);
+#pragma unroll
+          for (int i = 0; i < KB; ++i) wv[u][i] = src[i];
+        }
+        sc[u] = f16_value(a.k_scale[irow * G + g]);
+        zp[u] = f16_value(a.k_zero[irow * G + g]);
+      }
+    });
+    static_for<kBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      // every lane takes part in the tile exchange; rows past the end compute
+      // on zeros and are not stored
+      const float s16 = act[u] ? canon_nan(sc[u]) : 0.f, z16 = act[u] ? canon_nan(zp[u]) : 0.f;
+      float k[32];
+      if constexpr (KB == 8) {
+        // idx + zero == (idx + 128) + (zero - 128) exactly: both are integers
+        // far below 2^24 (or zero is infinite/NaN, which both forms carry)
+        const float zb = z16 - 128.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b = wv[u][i] ^ 0x80808080u;
+          k[4 * i] = ((float)(b & 0xFFu) + zb) * s16;
+          k[4 * i + 1] = ((float)((b >> 8) & 0xFFu) + zb) * s16;
+          k[4 * i + 2] = ((float)((b >> 16) & 0xFFu) + zb) * s16;
+          k[4 * i + 3] = ((float)((b >> 24) & 0xFFu) + zb) * s16;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int bit = KB * i, wd = bit >> 5, off = bit & 31;
+          uint32_t v = wv[u][wd] >> off;
+          if (off + KB > 32) v |= wv[u][wd + 1] << (32 - off);
+          k[i] = ((float)(v & ((1u << KB) - 1)) + z16) * s16;
+        }
+      }
+      uint32_t o[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] = pack_bf16x2(k[2 * i], k[2 * i + 1]);
+      store_tile<D>(o, a.k, act[u] ? orow[u] * D : -1, tile, offs, lane, g, rw);
+    });
   }
+}
+
+// One value group back to bf16: centroid lookup, scale, transform,
+// 1/sqrt(d), signs (applied to the rounded bf16 pair: an exact sign flip).
+// CANON rewrites NaN halves to 0x7FC0 after the sign flip.
+template <int D, int VB, bool CANON>
+__device__ __forceinline__ void dequant_value_group(const uint32_t (&wv)[VB], float sc, const float* cen,
+                                                    const uint32_t (&smask)[16], float rd, int lane,
+                                                    int g, int rw, uint16_t* base, int64_t off,
+                                                    uint8_t* tile, int64_t* offs) {
+  float z[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int bit = VB * i, wd = bit >> 5, off = bit & 31;
+    uint32_t v;
+    if (off + VB <= 32)
+      v = __builtin_amdgcn_ubfe(wv[wd], off, VB);
+    else
+      v = (wv[wd] >> off) | ((wv[wd + 1] << (32 - off)) & ((1u << VB) - 1));
+    z[i] = cen[v] * sc;
+  }
+  const float m = fwht_group<D>(z, lane) * rd;
+  uint32_t o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = pack_bf16x2(z[2 * i] * m, z[2 * i + 1] * m) ^ smask[i];
+  if constexpr (CANON) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t lo = o[i] & 0xFFFFu, hi = o[i] >> 16;
+      o[i] = (((lo & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : lo) | ((((hi & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : hi) << 16);
+    }
+  }
+  store_tile<D>(o, base, off, tile, offs, lane, g, rw);
 }
 
 template <int D, int VB>
 __device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uint32_t blk, uint32_t nblk) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR, G = D / kGroup;
+  using L = GroupLanes<D>;
+  constexpr int G = D / kGroup;
   __shared__ float cen_lds[1 << VB];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][kTileBytes];
+  __shared__ int64_t row_offs[4][L::RPW];
   for (int i = threadIdx.x; i < (1 << VB); i += blockDim.x)
     cen_lds[i] = __uint_as_float(centroids<VB>()[i]);
   __syncthreads();
-  const int lane = threadIdx.x & 63, sub = lane % LPR, rw = lane / LPR;
+  const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
+  uint8_t* tile = tiles[threadIdx.x >> 6];
+  int64_t* offs = row_offs[threadIdx.x >> 6];
   const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
-  const uint32_t nwave = nblk * 4u;
-  float sg[8];
-  lane_signs(a.signs, sub, sg);
+  const uint32_t step = nblk * 4u * L::RPW;
+  uint32_t smask[16];
+  {
+    const uint4* sp = reinterpret_cast<const uint4*>(a.signs + kGroup * g);
+    const uint4 s0 = sp[0], s1 = sp[1];
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t word = sw[i >> 1] >> (16 * (i & 1));
+      smask[i] = ((word & 0x80u) << 8) | ((word & 0x8000u) << 16);
+    }
+  }
   const float rd = inv_sqrt_d<D>();
-  for (uint32_t base = wave * RPW; base < a.rows; base += nwave * RPW) {
-    const uint32_t r = base + rw;
-    const bool active = r < a.rows;
-    uint32_t s, t, h;
-    split_row(active ? r : 0u, a.split, s, t, h);
-    const int64_t irow = row_index(a.in, s, t, h), orow = row_index(a.out, s, t, h);
-    uint64_t bits = 0;
-    float sc = 0.f;
-    if (active) {
-      bits = load_lane_bits<VB>(a.v_q + irow * (D * VB / 8), sub);
-      sc = canon_nan(f16_value(a.v_scale[irow * G + (sub >> 2)]));
-    }
-    float z[8];
+  for (uint32_t base = wave * L::RPW; base < a.rows; base += kBatch * step) {
+    uint32_t wv[kBatch][VB];
+    float scb[kBatch];
+    int64_t orow[kBatch];
+    bool act[kBatch];
+    static_for<kBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const uint32_t r = base + u * step + rw;
+      act[u] = r < a.rows;
+      uint32_t s, t, h;
+      split_row(act[u] ? r : 0u, a.split, s, t, h);
+      const int64_t irow = row_index(a.in, s, t, h);
+      orow[u] = row_index(a.out, s, t, h);
+      scb[u] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = cen_lds[(bits >> (VB * i)) & ((1u << VB) - 1)] * sc;
-    fwht_row<D>(z, sub);
+      for (int i = 0; i < VB; ++i) wv[u][i] = 0;
+      if (act[u]) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.v_q + irow * (D * VB / 8) + 4 * VB * g);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = (z[i] * rd) * sg[i];
-    if (active) {
-      uint4 o;
-      o.x = pack_bf16x2(z[0], z[1]);
-      o.y = pack_bf16x2(z[2], z[3]);
-      o.z = pack_bf16x2(z[4], z[5]);
-      o.w = pack_bf16x2(z[6], z[7]);
-      *reinterpret_cast<uint4*>(a.v + orow * D + 8 * sub) = o;
-    }
+        for (int i = 0; i < VB; ++i) wv[u][i] = src[i];
+        scb[u] = f16_value(a.v_scale[irow * G + g]);
+      }
+    });
+    static_for<kBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      // the transform needs every lane of the row: inactive rows compute on
+      // zeros and skip the store.  Only a non-finite scale can produce NaN;
+      // such rows take the variant that keeps every NaN at 0x7FC0.
+      const float sc = canon_nan(scb[u]);
+      if (__any(!__builtin_isfinite(sc)))
+        dequant_value_group<D, VB, true>(wv[u], sc, cen_lds, smask, rd, lane, g, rw, a.v,
+                                         act[u] ? orow[u] * D : -1, tile, offs);
+      else
+        dequant_value_group<D, VB, false>(wv[u], sc, cen_lds, smask, rd, lane, g, rw, a.v,
+                                          act[u] ? orow[u] * D : -1, tile, offs);
+    });
   }
 }
 
@@ -302,10 +634,10 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
 }
 
 // ------------------------------------------------------------- dispatch
-// Blocks per half: enough 16-row chunks to cover the rows, capped so a block
-// loops over several chunks on large inputs.
+// Blocks per half: enough to cover the rows (4 waves of 64*32/d rows each),
+// capped so a block loops over several chunks on large inputs.
 static unsigned blocks_per_half(uint32_t rows, int d, int max_blocks) {
-  const uint32_t rows_per_block = 4u * (64u * 8u / (uint32_t)d);
+  const uint32_t rows_per_block = 4u * (64u * 32u / (uint32_t)d);
   uint32_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks > (uint32_t)max_blocks) blocks = (uint32_t)max_blocks;
   return blocks < 1 ? 1u : blocks;

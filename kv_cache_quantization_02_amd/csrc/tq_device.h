@@ -35,11 +35,12 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// bf16 pair (round to nearest even by the hardware converter).
+// bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+typedef float tq_float2 __attribute__((ext_vector_type(2)));
+typedef __bf16 tq_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const tq_float2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, tq_bf16x2));
 }
 
 // fp16 pattern of a float, round to nearest even; every NaN -> 0x7E00.
