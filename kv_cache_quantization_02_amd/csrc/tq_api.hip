@@ -190,7 +190,7 @@ size_t tq_decode_attn_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t
   if (check_scheme(s) != TQ_OK) return 0;
   if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1) return 0;
   int splits = 0, tps = 0;
-  tq::decode_attn_geometry(s->head_dim, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
+  tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
   return tq::decode_attn_part_bytes(s->head_dim, batch, n_q_heads, splits);
 }
 
@@ -210,7 +210,7 @@ int32_t tq_decode_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t
   if ((st = check_planes(cache)) != TQ_OK) return st;
   if (!aligned16(q_bf16) || !aligned16(signs) || !aligned16(out_bf16)) return TQ_E_ALIGN;
   int splits = 0, tps = 0;
-  tq::decode_attn_geometry(s->head_dim, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
+  tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
   if (!workspace || workspace_bytes < tq::decode_attn_part_bytes(s->head_dim, batch, n_q_heads, splits))
     return TQ_E_WORKSPACE;
   if (!aligned16(workspace)) return TQ_E_ALIGN;

@@ -39,6 +39,7 @@ __device__ __forceinline__ const uint32_t* attn_centroids() {
 constexpr int kHeadTile = 4;   // query heads per block
 constexpr int kChunk = 4;      // rows per lane-group between softmax rescales
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;  // log2 slack of the matrix-core kernel's running maximum
 
 // One split partial per (sequence, query head): acc[d], m, l, two pad words
 // (keeps every record 16-byte aligned).
@@ -228,25 +229,54 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
 //
 // Both contractions run on v_mfma_f32_16x16x32_f16 (gfx950 operand layout:
 // A[l%16][8(l/16)+i], B[8(l/16)+i][l%16], D[4(l/16)+i][l%16] for lane l).
-// A wave takes 32 cached tokens per step for a tile of 4 query heads.
-//  * QK^T: a key byte b = idx ^ 0x80 becomes the exact fp16 1024 + (idx+128),
-//    so each 32-element group g contributes
-//        s_g * (sum_j q_j (1024 + u_j) + (zero_g - 1152) * sum_j q_j),
-//    i.e. idx + zero times the fp16 scale.  A is block-diagonal over 4 groups
-//    (rows 4g + h), so all 16 output rows are used; the 4 lane-groups'
-//    per-group partials are then summed with three permlane swaps, leaving
-//    lane-group h with head h's scores.
-//  * Online softmax per head in the log2 domain (q carries
-//    softmax_scale * log2 e), exact rescaling whenever the maximum moves.
-//  * PV: the 32 value rows are decoded once into LDS as fp16 centroids
-//    (a lookup of two indices at a time), and A = p * value-scale (fp16, block-
-//    diagonal over four 8-token sub-chunks) multiplies them: the rotated-domain
-//    accumulation z = centroid * scale, with the scale folded into the weights.
-// The per-split (m, l, acc) partials match the VALU kernel's, so the same
-// combine kernel applies the inverse rotation.
+// A block of four waves serves one (sequence, kv head, tile of four query
+// heads, context split); each wave takes 32 cached tokens per step.
+//
+// Memory: every byte a step reads (key rows, packed value rows, the three
+// fp16 planes of its 32 tokens) is copied HBM -> LDS by global_load_lds DMA
+// into per-wave stage buffers, S-1 steps ahead of use.  The copies hold no
+// registers, so each wave keeps S-1 steps of loads in flight while it
+// computes.  Stage layouts are chosen per DMA lane (the LDS side of a DMA is
+// fixed at base + 4 * size * lane), so every lane's global offset depends on
+// the lane only, except in the final partial step, whose rows beyond the
+// context are clamped to its last row (their scores are masked and their
+// value scales zeroed).
+//  * QK^T: a key byte b (two's complement index) becomes the exact fp16
+//    1024 + (b ^ 0x80); a group's contraction gives sum_j q_j (1152 + idx_j),
+//    and scale * (idx + zero) . q follows with the group sums of q.  A is
+//    block-diagonal over four groups (row 4 (g mod 4) + h); a lane's 16-byte
+//    key chunk feeds two MFMAs, and A routes each element to its group's row.
+//    Three permlane swaps sum the lane-groups' partials per head.
+//  * The query is scaled by softmax_scale * log2 e and by a per-head power of
+//    two that puts its largest element in [1/2, 1) before the fp16
+//    conversion; the scores are scaled back exactly.
+//  * Online softmax per head in the log2 domain, exact rescaling whenever
+//    the running maximum moves.
+//  * PV: A = p * value scale, B = fp16 centroids, accumulated in the rotated
+//    domain.  The value scales of group g are multiplied by 2^-E_g, E_g the
+//    least power of two above every scale of that group the wave has seen,
+//    so the fp16 product never overflows and only terms below 2^-24 of the
+//    largest lose bits; the group's accumulators are rescaled exactly when
+//    E_g grows.  Column n of group g's two output tiles holds dims
+//    32g + 2n and 32g + 2n + 1, so a lane's two indices per token are
+//    adjacent bits of the packed row and one lookup yields both centroids.
+//    Contraction index k = 8c + i stands for token c + 4i of the step, which
+//    puts the four lane-groups' reads of the packed rows on distinct banks.
+// The per-split (m, l, acc) partials are what the combine kernel expects.
 typedef _Float16 tq_half8 __attribute__((ext_vector_type(8)));
 typedef float tq_float4 __attribute__((ext_vector_type(4)));
 typedef _Float16 tq_half2 __attribute__((ext_vector_type(2)));
+typedef unsigned short tq_ushort2 __attribute__((ext_vector_type(2)));
+typedef int tq_i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef uint32_t tq_u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tq_u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) tq_i32x4 lds_i32x4;
+typedef __attribute__((address_space(3))) tq_float4 lds_f32x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -278,20 +308,128 @@ __device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(tq_half2, a) * __builtin_bit_cast(tq_half2, b));
 }
 
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(tq_ushort2, a),
+                                                                __builtin_bit_cast(tq_ushort2, b)));
+}
+
+// max over the lanes that share lane % M0 (M0 a power of two below 64)
+template <int M>
+__device__ __forceinline__ uint32_t xor_max_from(uint32_t v) {
+  if constexpr (M < 64) {
+    v = pk_max_u16(v, __float_as_uint(lane_xor<M>(__uint_as_float(v))));
+    return xor_max_from<2 * M>(v);
+  } else {
+    return v;
+  }
+}
+
+// fp16 pattern of 2^-e for e in [-13, 17] (the last three are subnormal)
+__device__ __forceinline__ uint32_t f16_pow2_neg(int e) {
+  return e <= 14 ? (uint32_t)(15 - e) << 10 : 1u << (24 - e);
+}
+
 template <int D, int VB>
-__global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
-  constexpr int G = D / kGroup, NSET = (G + 3) / 4, NT = D / 16;
-  constexpr int CH = 32;                    // tokens per step: the PV MFMA depth
-  constexpr int ZS = 2 * D + 16;            // LDS bytes per decoded row (padded)
-  constexpr int LW = D * VB / 64;           // packed dwords per decode lane
-  constexpr int PB = 4 * CH;                // p[h][t] floats, then 8 zeros
-  constexpr int VROW = D * VB / 8;
-  constexpr int ACC_BYTES = 4 * NT * 4 * 64 * 4;
-  constexpr int ZB_BYTES = 4 * CH * ZS > ACC_BYTES ? 4 * CH * ZS : ACC_BYTES;
-  __shared__ uint32_t lut[1 << (2 * VB)];
-  __shared__ __attribute__((aligned(16))) uint8_t zb_all[ZB_BYTES];
-  __shared__ __attribute__((aligned(16))) float pb_all[4][PB + 8];
-  __shared__ float stats[4][4][2];
+struct MfmaCfg {
+  static constexpr int G = D / kGroup, GW = G / 2, NSET = (G + 3) / 4, NT = D / 16, CH = 32;
+  static constexpr int CPR = D / 16, SW = CPR < 8 ? CPR : 8;  // key chunks per row, swizzle span
+  static constexpr int W = D * VB / 32;                      // packed value dwords per row
+  static constexpr int NK = CH * D / 1024;                   // 16-byte DMAs of key rows
+  static constexpr int NV = CH * W / 64;                     // 4-byte DMAs of value rows
+  static constexpr int SC_DW = CH * GW, NSP = (SC_DW + 63) / 64;  // per fp16 plane
+  static constexpr int NI = NK + NV + 3 * NSP;               // DMA instructions per step
+  static constexpr int OFF_V = CH * D;
+  static constexpr int OFF_KS = OFF_V + NV * 256;
+  static constexpr int OFF_KZ = OFF_KS + NSP * 256;
+  static constexpr int OFF_VS = OFF_KZ + NSP * 256;
+  static constexpr int STAGE = OFF_VS + NSP * 256;
+  static constexpr int PB = 4 * CH;   // p[head][slot], then 32 zeros
+  static constexpr int LUT = 1 << (2 * VB);
+  static constexpr int OFF_PB = LUT * 4 > 256 ? LUT * 4 : 256;
+  static constexpr int OFF_STATS = OFF_PB + 4 * (PB + 32) * 4;
+  static constexpr int OFF_BUF = OFF_STATS + 4 * 4 * 2 * 4;
+  static constexpr int EXTRA = OFF_BUF + 1024;
+  // three stages when two blocks still fit a CU, else two
+  static constexpr int S = (4 * 3 * STAGE + EXTRA <= 81920 && 2 * NI <= 63) ? 3 : 2;
+  static constexpr int ACC_BYTES = 4 * NT * 4 * 64 * 4;
+  static constexpr int BUF = (4 * S * STAGE > ACC_BYTES) ? 4 * S * STAGE : ACC_BYTES;
+  static_assert(G % 2 == 0 && (CH * W) % 64 == 0 && (CH * D) % 1024 == 0, "step layout");
+  static_assert((S - 1) * NI <= 63, "vmcnt range");
+};
+
+// One DMA instruction: each lane copies `size` bytes from base + voff to LDS
+// byte lds + size * lane.  Written as inline assembly so that the compiler
+// neither tracks these LDS writes (it would wait for every outstanding copy
+// before each LDS read) nor moves them; completion is awaited explicitly with
+// s_waitcnt vmcnt before a stage is read.  M0 (the LDS base of the copy) is
+// reserved by the compiler and read by no other instruction of this kernel;
+// each statement sets it immediately before its own copy.
+__device__ __forceinline__ void dma_x4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_x1(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
+
+// Issue the DMAs of the step whose first row is r0 into `stage`.  TAIL: only
+// the first tl rows are inside the context; later rows re-read row tl - 1.
+template <int D, int VB, bool TAIL>
+__device__ __forceinline__ void attn_dma(const AttnArgs& a, lds_u8* stage, int64_t r0, int tl, int lane) {
+  using C = MfmaCfg<D, VB>;
+  const uint8_t* kb = a.k_q + r0 * D;
+#pragma unroll
+  for (int j = 0; j < C::NK; ++j) {
+    const int s = 64 * j + lane;
+    int t = s / C::CPR;
+    const int ch = (s % C::CPR) ^ (t & (C::SW - 1));
+    if (TAIL) t = min(t, tl - 1);
+    dma_x4(kb, (uint32_t)(t * D + 16 * ch), lds_addr(stage + 1024 * j));
+  }
+  const uint8_t* vb = a.v_q + r0 * (4 * C::W);
+#pragma unroll
+  for (int j = 0; j < C::NV; ++j) {
+    const int s = 64 * j + lane;
+    int off = 4 * s;
+    if (TAIL) {
+      const int t = s / C::W;
+      off = 4 * (min(t, tl - 1) * C::W + (s - t * C::W));
+    }
+    dma_x1(vb, (uint32_t)off, lds_addr(stage + C::OFF_V + 256 * j));
+  }
+  const uint16_t* planes[3] = {a.k_scale, a.k_zero, a.v_scale};
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const uint16_t* pbase = planes[p] + r0 * C::G;
+#pragma unroll
+    for (int j = 0; j < C::NSP; ++j) {
+      int s = 64 * j + lane;
+      if (s >= C::SC_DW) s = C::SC_DW - 1;
+      int t = s / C::GW;
+      const int w = s - t * C::GW;
+      if (TAIL) t = min(t, tl - 1);
+      dma_x1(pbase, (uint32_t)(4 * (t * C::GW + w)), lds_addr(stage + C::OFF_KS + p * C::NSP * 256 + 256 * j));
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D, int VB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_attn_mfma_kernel(AttnArgs a) {
+  using C = MfmaCfg<D, VB>;
+  constexpr int G = C::G, GW = C::GW, NSET = C::NSET, NT = C::NT, CH = C::CH, W = C::W, S = C::S;
+  // one LDS block: the centroid-pair table first (its byte offsets are the
+  // masked index bits themselves), then p, the merge statistics, the stages
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[C::OFF_BUF + C::BUF];
+  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(lds_all);
+  float(*const stats)[4][2] = reinterpret_cast<float(*)[4][2]>(lds_all + C::OFF_STATS);
+  uint8_t* const smem = lds_all + C::OFF_BUF;
 
   const int split = blockIdx.x % a.splits;
   int rest = blockIdx.x / a.splits;
@@ -301,18 +439,20 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
   rest /= tiles;
   const int gkv = rest % a.n_kv_heads;
   const int b = rest / a.n_kv_heads;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
   const int c = lane >> 4, n = lane & 15, r = n >> 2, hh = n & 3;
-  uint8_t* zb = zb_all + wave * CH * ZS;
-  float* pb = pb_all[wave];
+  lds_u8* const wbuf = (lds_u8*)smem + wave * S * C::STAGE;
+  lds_f32* const pb = (lds_f32*)(lds_all + C::OFF_PB) + wave * (C::PB + 32);
+  lds_u8* const lut = (lds_u8*)lds_all;
 
-  for (int i = threadIdx.x; i < (1 << (2 * VB)); i += blockDim.x) {
+  for (int i = threadIdx.x; i < C::LUT; i += blockDim.x) {
     const uint32_t* cen = attn_centroids<VB>();
     const float c0 = __uint_as_float(cen[i & ((1 << VB) - 1)]);
     const float c1 = __uint_as_float(cen[i >> VB]);
-    lut[i] = half2_bits(c0, c1);
+    lut_s[i] = half2_bits(c0, c1);
   }
-  if (lane < 8) pb[PB + lane] = 0.f;
+  if (lane < 32) pb[C::PB + lane] = 0.f;
 
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
@@ -321,8 +461,18 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
   if (t_end > ctx) t_end = ctx;
   const int64_t row0 = (int64_t)b * a.seq_stride + (int64_t)gkv * a.head_stride;
 
-  // ---- query: block-diagonal A operands (lane (n = 4r + h, c) carries head h
-  // for the group with g % 4 == r) and per-group sums for the zero term
+  // start the first S-1 steps' copies before the query set-up
+  const int first = t_begin + wave * CH;
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) {
+    const int cb = first + 4 * CH * k;
+    if (cb + CH <= t_end)
+      attn_dma<D, VB, false>(a, wbuf + k * C::STAGE, row0 + cb, CH, lane);
+    else if (cb < t_end)
+      attn_dma<D, VB, true>(a, wbuf + k * C::STAGE, row0 + cb, t_end - cb, lane);
+  }
+
+  // ---- query
   const float qscale = a.softmax_scale * kLog2e;
   auto qhead = [&](int h) -> const uint16_t* {
     const int hl = tile * kHeadTile + h;
@@ -330,25 +480,62 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
     return a.q + ((int64_t)b * a.n_q_heads + hq) * D;
   };
   auto hvalid = [&](int h) { return tile * kHeadTile + h < rep; };
-  tq_half8 aq[G];
+  // per-head power of two (lane-group c measures head c)
+  float qmax = 0.f;
+  if (hvalid(c)) {
+    const uint16_t* qp = qhead(c) + n * (D / 16);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const bool on = ((g & 3) == r) && hvalid(hh);
-    const uint4 w = on ? *reinterpret_cast<const uint4*>(qhead(hh) + kGroup * g + 8 * c) : make_uint4(0, 0, 0, 0);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      aq[g][2 * i] = (_Float16)(bf16_lo(ws[i]) * qscale);
-      aq[g][2 * i + 1] = (_Float16)(bf16_hi(ws[i]) * qscale);
+    for (int i = 0; i < D / 16; i += 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(qp + i);
+      qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
     }
   }
+  qmax = row16_max(qmax) * fabsf(qscale);
+  int qe = 0;
+  (void)frexpf(qmax, &qe);
+  qe = qe < -100 ? -100 : (qe > 100 ? 100 : qe);
+  // The query enters the int8 MFMA as the exact pair hi * 256 + lo of the
+  // fixed-point value q * softmax_scale * log2 e * 2^(14 - qe), |.| <= 2^14,
+  // hi in [-64, 64], lo in [-128, 127]; the key bytes are the B operand as
+  // stored.  Scores come back to scale through 2^(qe - 14).
+  const float smul = ldexpf(1.f, qe - 14);
+  float qn[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) qn[h] = ldexpf(qscale, 14 - __builtin_amdgcn_readlane(qe, 16 * h));
+  const float qn_l = hh == 0 ? qn[0] : (hh == 1 ? qn[1] : (hh == 2 ? qn[2] : qn[3]));
+  auto qfix = [](float x) { return (int)__builtin_rintf(x); };
+  // A operands: MFMA gp takes key bytes 64gp + 16c + i (i < 16), of group
+  // 2gp + c/2, routed to row 4 ((2gp + c/2) mod 4) + h
+  tq_i32x4 aqh[G / 2], aql[G / 2];
+#pragma unroll
+  for (int gp = 0; gp < G / 2; ++gp) {
+    const int g = 2 * gp + (c >> 1);
+    const bool on = ((g & 3) == r) && hvalid(hh);
+    const uint16_t* qp = qhead(hh) + 64 * gp + 16 * c;
+    const uint4 w0 = on ? *reinterpret_cast<const uint4*>(qp) : make_uint4(0, 0, 0, 0);
+    const uint4 w1 = on ? *reinterpret_cast<const uint4*>(qp + 8) : make_uint4(0, 0, 0, 0);
+    const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = (i & 1) ? bf16_hi(ws[i >> 1]) : bf16_lo(ws[i >> 1]);
+      const int v = qfix(x * qn_l);
+      const int lo = ((v + 128) & 255) - 128;
+      const int hi = (v - lo) >> 8;
+      hw[i >> 2] |= (uint32_t)(hi & 255) << (8 * (i & 3));
+      lw[i >> 2] |= (uint32_t)(lo & 255) << (8 * (i & 3));
+    }
+    aqh[gp] = tq_i32x4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+    aql[gp] = tq_i32x4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
+  }
+  // per-group sums of the fixed-point query (exact integers)
   float qsum[NSET][4];
 #pragma unroll
   for (int st = 0; st < NSET; ++st) {
     const int g = 4 * st + c;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      float acc = 0.f;
+      int acc = 0;
       if (g < G && hvalid(h)) {
         const uint4* p = reinterpret_cast<const uint4*>(qhead(h) + kGroup * g);
 #pragma unroll
@@ -356,84 +543,138 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
           const uint4 w = p[j];
           const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc += (float)(_Float16)(bf16_lo(ws[i]) * qscale);
-            acc += (float)(_Float16)(bf16_hi(ws[i]) * qscale);
-          }
+          for (int i = 0; i < 4; ++i) acc += qfix(bf16_lo(ws[i]) * qn[h]) + qfix(bf16_hi(ws[i]) * qn[h]);
         }
       }
-      qsum[st][h] = acc;
+      qsum[st][h] = (float)acc;
     }
   }
+  // value fields: dims 32g + 2n, +1 sit at bits 2VB n of group g's segment;
+  // read the dword pair whose funnel shift leaves them at bit 2
+  int fk = (2 * VB * n) >> 5, fsh = (2 * VB * n) & 31;
+  if (fsh < 2) {
+    fk -= 1;
+    fsh += 30;
+  } else {
+    fsh -= 2;
+  }
+  const int vdw = C::OFF_V / 4 + c * W + fk;  // + 4W i + VB g for token c + 4i, group g
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
   tq_float4 acc[NT];
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) acc[jt] = tq_float4{0.f, 0.f, 0.f, 0.f};
+  int E[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) E[g] = -13;
 
-  for (int cb = t_begin + wave * CH; cb < t_end; cb += 4 * CH) {
-    // ---- decode the 32 value rows of this step into LDS (fp16, row-major)
+  int slot = 0;
+  for (int cb = first; cb < t_end; cb += 4 * CH) {
+    // copies of the step S-1 ahead go into the slot freed by the previous step
+    const int cbn = cb + 4 * CH * (S - 1);
+    const int nslot = slot == 0 ? S - 1 : slot - 1;
+    if (cbn + CH <= t_end)
+      attn_dma<D, VB, false>(a, wbuf + nslot * C::STAGE, row0 + cbn, CH, lane);
+    else if (cbn < t_end)
+      attn_dma<D, VB, true>(a, wbuf + nslot * C::STAGE, row0 + cbn, t_end - cbn, lane);
+    const int later = (t_end - cb - 1) / (4 * CH);  // steps after this one
+    if (later >= 2 && S == 3)
+      wait_vmcnt<(S - 1) * C::NI>();
+    else if (later >= 1)
+      wait_vmcnt<C::NI>();
+    else
+      wait_vmcnt<0>();
+
+    lds_u8* const sp = wbuf + slot * C::STAGE;
+    slot = slot == S - 1 ? 0 : slot + 1;
+    const int tl = t_end - cb;
+    const bool full = tl >= CH;
+
+    // ---- value scales: zero rows past the context, track E_g, normalise,
+    // and rewrite them in place as fp16 pairs (slot 2k, slot 2k+1) per group,
+    // slot 8 (t mod 4) + t / 4 for token t: the A operand of PV reads them as is
     {
-      const int tt = lane >> 1, half = lane & 1;
-      const int t = cb + tt;
-      uint32_t wv[LW];
-      if (t < t_end) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.v_q + (row0 + t) * VROW + half * (VROW / 2));
+      lds_u32* const vs = (lds_u32*)(sp + C::OFF_VS);
+      constexpr int PER = (C::SC_DW + 63) / 64;
+      uint32_t x[PER], mx = 0;
 #pragma unroll
-        for (int i = 0; i < LW; ++i) wv[i] = src[i];
+      for (int k = 0; k < PER; ++k) {
+        const int d = lane + 64 * k;
+        x[k] = d < C::SC_DW ? vs[d] : 0u;
+        if (!full && d / GW >= tl) x[k] = 0u;
+        mx = pk_max_u16(mx, x[k] & 0x7FFF7FFFu);
       }
-      uint8_t* zrow = zb + tt * ZS + half * D;
+      mx = xor_max_from<GW>(mx);
+      uint32_t rp[GW];
 #pragma unroll
-      for (int q4 = 0; q4 < D / 16; ++q4) {
-        uint32_t o[4];
+      for (int w = 0; w < GW; ++w) {
+        const uint32_t mw = __builtin_amdgcn_readlane(mx, w);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int p = 4 * q4 + k, bit = 2 * VB * p, wd = bit >> 5, off = bit & 31;
-          uint32_t f;
-          if (off + 2 * VB <= 32)
-            f = __builtin_amdgcn_ubfe(wv[wd], off, 2 * VB);
-          else
-            f = (wv[wd] >> off) | ((wv[wd + 1] << (32 - off)) & ((1u << (2 * VB)) - 1));
-          o[k] = (t < t_end) ? lut[f] : 0u;
+        for (int hf = 0; hf < 2; ++hf) {
+          const int g = 2 * w + hf;
+          const int ex = (int)((mw >> (16 * hf + 10)) & 31u);
+          const int en = (ex > 1 ? ex : 1) - 14;
+          if (en > E[g]) {
+            const float f = ldexpf(1.f, E[g] - en);
+            acc[2 * g] *= f;
+            acc[2 * g + 1] *= f;
+            E[g] = en;
+          }
         }
-        *reinterpret_cast<uint4*>(zrow + 16 * q4) = make_uint4(o[0], o[1], o[2], o[3]);
+        rp[w] = f16_pow2_neg(E[2 * w]) | (f16_pow2_neg(E[2 * w + 1]) << 16);
+      }
+      lds_u16* const vs16 = (lds_u16*)vs;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int d = lane + 64 * k;
+        const int t = d / GW, w = d % GW;
+        uint32_t rpl = rp[0];
+#pragma unroll
+        for (int i = 1; i < GW; ++i)
+          if (w == i) rpl = rp[i];
+        const uint32_t y = pk_mul_f16(x[k], rpl);
+        const int u = 8 * (t & 3) + (t >> 2);
+        const int o = 2 * ((u >> 1) * G + 2 * w) + (u & 1);
+        if (d < C::SC_DW) {
+          vs16[o] = (uint16_t)y;
+          vs16[o + 2] = (uint16_t)(y >> 16);
+        }
       }
     }
+
     // ---- scores for the two 16-token tiles
-    float S[2];
+    const lds_u16* const ks = (const lds_u16*)(sp + C::OFF_KS);
+    const lds_u16* const kz = (const lds_u16*)(sp + C::OFF_KZ);
+    float Sc[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const int t = cb + 16 * tau + n;
-      const bool tv = t < t_end;
-      const int64_t row = row0 + t;
+      const int t = 16 * tau + n;
       float T[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NSET; ++st) {
-        tq_float4 d = {0.f, 0.f, 0.f, 0.f};
+        tq_i32x4 dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
 #pragma unroll
-        for (int gi = 0; gi < 4 && 4 * st + gi < G; ++gi) {
-          const int g = 4 * st + gi;
-          uint2 kw = make_uint2(0x80808080u, 0x80808080u);
-          if (tv) kw = *reinterpret_cast<const uint2*>(a.k_q + row * D + kGroup * g + 8 * c);
-          const uint32_t u0 = kw.x ^ 0x80808080u, u1 = kw.y ^ 0x80808080u;
-          uint32_t bw[4];
-          bw[0] = __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u);
-          bw[1] = __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u);
-          bw[2] = __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u);
-          bw[3] = __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u);
-          const tq_half8 bk = __builtin_bit_cast(tq_half8, bw);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, d, 0, 0, 0);
+        for (int gq = 0; gq < 2; ++gq) {
+          const int gp = 2 * st + gq;
+          if (gp < G / 2) {
+            const int ch = 4 * gp + c;
+            const tq_i32x4 kw = *(const lds_i32x4*)(sp + 16 * (t * C::CPR + (ch ^ (t & (C::SW - 1)))));
+            dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(aqh[gp], kw, dh, 0, 0, 0);
+            dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(aql[gp], kw, dl, 0, 0, 0);
+          }
         }
         const int g = 4 * st + c;
         float sk = 0.f, zk = 0.f;
-        if (tv && g < G) {
-          sk = f16_value(a.k_scale[row * G + g]);
-          zk = f16_value(a.k_zero[row * G + g]);
+        if (g < G) {
+          sk = f16_value(ks[t * G + g]);
+          zk = f16_value(kz[t * G + g]);
         }
-        const float zq = zk - 1152.0f;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) T[h] = __builtin_fmaf(sk, __builtin_fmaf(zq, qsum[st][h], d[h]), T[h]);
+        for (int h = 0; h < 4; ++h) {
+          const float d = (float)(dh[h] * 256 + dl[h]);  // exact: |.| < 2^29
+          T[h] = __builtin_fmaf(sk, __builtin_fmaf(zk, qsum[st][h], d), T[h]);
+        }
       }
       // lane-group h collects head h: sum over the four lane-groups
       const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[0]), __float_as_uint(T[2]), false, false);
@@ -441,22 +682,28 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
       const float a02 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
       const float a13 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
       const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(a02), __float_as_uint(a13), false, false);
-      const float sc = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-      S[tau] = tv ? sc : -INFINITY;
+      const float sc = (__uint_as_float(y[0]) + __uint_as_float(y[1])) * smul;
+      Sc[tau] = (full || t < tl) ? sc : -INFINITY;
     }
     // ---- online softmax for head c (lane-group c)
-    const float cm = row16_max(fmaxf(S[0], S[1]));
-    const float m_new = fmaxf(m_run, cm);
+    // The reference m_run moves only when a score exceeds it by more than
+    // 2^kLazy (or on the first scores), so p <= 2^kLazy stays well inside
+    // fp16 and the accumulators are rarely rescaled; the result is the same
+    // ratio of sums.
+    const float cm = row16_max(fmaxf(Sc[0], Sc[1]));
+    const float m_new = (cm > m_run + kLazy) ? cm : m_run;
     float alpha = 1.f, p0 = 0.f, p1 = 0.f;
     if (m_new != -INFINITY) {
-      alpha = exp2f(m_run - m_new);
-      p0 = exp2f(S[0] - m_new);
-      p1 = exp2f(S[1] - m_new);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      p0 = __builtin_amdgcn_exp2f(Sc[0] - m_new);
+      p1 = __builtin_amdgcn_exp2f(Sc[1] - m_new);
     }
     l_run = l_run * alpha + row16_sum(p0 + p1);
     m_run = m_new;
-    pb[c * CH + n] = p0;
-    pb[c * CH + 16 + n] = p1;
+    // token t sits at contraction slot 8 (t mod 4) + t / 4
+    const int sl = 8 * (n & 3) + (n >> 2);
+    pb[c * CH + sl] = p0;
+    pb[c * CH + sl + 4] = p1;
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -466,59 +713,67 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // ---- PV: A = p * value scale (fp16), block-diagonal over 8-token sub-chunks
+
+    // ---- PV.  A (lanes on the diagonal r == c): p * normalised scale of
+    // tokens c + 4i; B: centroids of those tokens at this lane's two dims
     const bool diag = (r == c);
-    const float* pp = diag ? pb + hh * CH + 8 * c : pb + PB;
-    const float4 pa = *reinterpret_cast<const float4*>(pp);
-    const float4 pc = *reinterpret_cast<const float4*>(pp + 4);
+    const lds_f32* pp = diag ? pb + hh * CH + 8 * c : pb + C::PB;
+    const tq_float4 pa = *(const lds_f32x4*)pp;
+    const tq_float4 pc = *(const lds_f32x4*)(pp + 4);
     const uint32_t ph[4] = {half2_bits(pa.x, pa.y), half2_bits(pa.z, pa.w), half2_bits(pc.x, pc.y),
                             half2_bits(pc.z, pc.w)};
-    // value scales of tokens cb+8c .. cb+8c+7, G fp16 each
-    uint32_t sv[8][(G + 1) / 2];
+    // (s[slot 2k][g], s[slot 2k+1][g]) for the slots 8c .. 8c+7 of this lane-group
+    const lds_u32* vsn = diag ? (const lds_u32*)(sp + C::OFF_VS) + 4 * c * G : (const lds_u32*)(pb + C::PB);
+    uint32_t sv[4][G];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int t = cb + 8 * c + k;
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int i = 0; i < (G + 1) / 2; ++i) sv[k][i] = 0;
-      if (diag && t < t_end) {
-        const uint32_t* sp = reinterpret_cast<const uint32_t*>(a.v_scale + (row0 + t) * G);
-#pragma unroll
-        for (int i = 0; i < G / 2; ++i) sv[k][i] = sp[i];
-      }
-    }
+      for (int g = 0; g < G; ++g) sv[k][g] = vsn[k * G + g];
+    // tokens c + 4i for i < 4 and i >= 4; the bases are pinned in registers
+    // so that every read of the pair below keeps an immediate offset
+    uint32_t va0 = lds_addr(sp) + 4u * (uint32_t)vdw, va1 = va0 + 64u * W;
+    asm volatile("" : "+v"(va0), "+v"(va1));
+    const lds_u32* const vrow0 = (const lds_u32*)(uintptr_t)va0;
+    const lds_u32* const vrow1 = (const lds_u32*)(uintptr_t)va1;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       uint32_t aw[4];
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        // (scale[2k2][g], scale[2k2+1][g]) as one fp16 pair
-        const uint32_t w0 = sv[2 * k2][g >> 1], w1 = sv[2 * k2 + 1][g >> 1];
-        const uint32_t spair = (g & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                       : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-        aw[k2] = pk_mul_f16(ph[k2], spair);
+      for (int k2 = 0; k2 < 4; ++k2) aw[k2] = pk_mul_f16(ph[k2], sv[k2][g]);
+      uint32_t L[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const lds_u32* f = (i < 4 ? vrow0 : vrow1) + 4 * W * (i & 3) + VB * g;
+        const uint32_t x = __builtin_amdgcn_alignbit(f[1], f[0], (uint32_t)fsh);
+        L[i] = *(const lds_u32*)(lut + (x & ((uint32_t)(C::LUT - 1) << 2)));
+      }
+      uint32_t b0[4], b1[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        b0[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x05040100u);
+        b1[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x07060302u);
       }
       const tq_half8 ap = __builtin_bit_cast(tq_half8, aw);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int jt = 2 * g + jj;
-        const uint16_t* zc = reinterpret_cast<const uint16_t*>(zb + (8 * c) * ZS) + 16 * jt + n;
-        uint32_t bw[4];
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2)
-          bw[k2] = (uint32_t)zc[(2 * k2) * (ZS / 2)] | ((uint32_t)zc[(2 * k2 + 1) * (ZS / 2)] << 16);
-        acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(tq_half8, bw), acc[jt], 0, 0, 0);
-      }
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(tq_half8, b0), acc[2 * g], 0, 0, 0);
+      acc[2 * g + 1] =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(tq_half8, b1), acc[2 * g + 1], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- merge lane-groups (token sub-chunks) and the four waves, write the split partial
+  // ---- back to true scale, merge lane-groups and waves, write the split partial
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float f = ldexpf(1.f, E[g]);
+    acc[2 * g] *= f;
+    acc[2 * g + 1] *= f;
+  }
   if (n == 0) {
     stats[wave][c][0] = m_run;
     stats[wave][c][1] = l_run;
   }
   __syncthreads();
-  float* accb = reinterpret_cast<float*>(zb_all);
+  lds_f32* const accb = (lds_f32*)smem;
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
@@ -531,7 +786,8 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(AttnArgs a) {
     for (int w = 0; w < 4; ++w) mm = fmaxf(mm, stats[w][h][0]);
     float ll = 0.f, aa = 0.f;
     if (mm != -INFINITY) {
-      const int jt = e >> 4, nn = e & 15;
+      // dim e = 32g + 2n + jj lives in tile 2g + jj, column n
+      const int jt = 2 * (e >> 5) + (e & 1), nn = (e & 31) >> 1;
       for (int w = 0; w < 4; ++w) {
         const float f = exp2f(stats[w][h][0] - mm);
         ll += stats[w][h][1] * f;
@@ -598,12 +854,21 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
   }
 }
 
-void decode_attn_geometry(int d, int batch, int n_q_heads, int n_kv_heads, int max_ctx, int* splits,
-                          int* tokens_per_split) {
-  const int step = 4 * (64 / (d / 8)) * kChunk;  // rows one block consumes per pass
+bool decode_attn_uses_mfma(int d, int kb, int vb) { return d <= 256 && kb == 8 && vb <= 5; }
+
+void decode_attn_geometry(int d, int kb, int vb, int batch, int n_q_heads, int n_kv_heads, int max_ctx,
+                          int* splits, int* tokens_per_split) {
+  // rows one block consumes per pass: four waves of 32-token steps on the
+  // matrix-core path, four waves of kChunk rows per lane-group otherwise
+  const bool mfma = decode_attn_uses_mfma(d, kb, vb);
+  const int step = mfma ? 4 * 32 : 4 * (64 / (d / 8)) * kChunk;
   const int rep = n_q_heads / n_kv_heads;
   const long long units = (long long)batch * n_kv_heads * ((rep + kHeadTile - 1) / kHeadTile);
-  long long s = (2048 + units - 1) / units;
+  // The matrix-core kernel streams through per-wave DMA stages, which pay a
+  // pipeline fill per block: aim at one round of resident blocks (two per CU
+  // on the 256 CUs of gfx950).  The VALU kernel prefers more, shorter blocks.
+  const long long target = mfma ? 512 : 2048;
+  long long s = (target + units - 1) / units;
   const long long max_s = (max_ctx + step - 1) / step;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
@@ -635,7 +900,11 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
   const int tiles = (rep + kHeadTile - 1) / kHeadTile;
   const dim3 grid((unsigned)(a.batch * a.n_kv_heads * tiles * a.splits));
   if constexpr (D <= 256) {
-    if (kb == 8 && vb <= 5) {
+    // the DMA copies need 16-byte key rows and 4-byte aligned fp16 planes
+    const bool aligned = ((uintptr_t)a.k_q & 15u) == 0 && ((uintptr_t)a.k_scale & 3u) == 0 &&
+                         ((uintptr_t)a.k_zero & 3u) == 0 && ((uintptr_t)a.v_scale & 3u) == 0 &&
+                         ((uintptr_t)a.v_q & 3u) == 0;
+    if (decode_attn_uses_mfma(D, kb, vb) && aligned) {
       switch (vb) {
         case 2: decode_attn_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(a); break;
         case 3: decode_attn_mfma_kernel<D, 3><<<grid, 256, 0, st>>>(a); break;

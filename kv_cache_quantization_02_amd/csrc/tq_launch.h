@@ -64,8 +64,9 @@ hipError_t launch_dequantize(const DequantArgs& a, int d, int kb, int vb, hipStr
 hipError_t launch_decode_attn(const AttnArgs& a, int d, int kb, int vb, hipStream_t st);
 
 // Split-K decode geometry for a given problem (shared by the workspace query).
-void decode_attn_geometry(int d, int batch, int n_q_heads, int n_kv_heads, int max_ctx, int* splits,
-                          int* tokens_per_split);
+bool decode_attn_uses_mfma(int d, int kb, int vb);
+void decode_attn_geometry(int d, int kb, int vb, int batch, int n_q_heads, int n_kv_heads, int max_ctx,
+                          int* splits, int* tokens_per_split);
 size_t decode_attn_part_bytes(int d, int batch, int n_q_heads, int splits);
 
 }  // namespace tq

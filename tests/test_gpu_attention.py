@@ -31,13 +31,33 @@ def _oracle_cache(k_bits_rows, v_bits_rows, signs, kb, vb, d):
     return khat, z
 
 
-def run_case(B, Hq, Hkv, N, d, kb, vb, ctx, seed, tag):
-    _say(f"[gpu attn] {tag}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} k{kb}v{vb} ctx={list(ctx)}")
+def _scaled(t, f):
+    return t if f == 1.0 else (t.float() * f).to(torch.bfloat16)
+
+
+def _misaligned(cache):
+    """Copies of the planes at base addresses that break the 16-byte (key
+    bytes) and 4-byte (fp16 planes) alignment of fresh allocations."""
+    out = {}
+    for name, t in cache.items():
+        shift = 8 if t.dtype == torch.uint8 else 1
+        buf = torch.empty(t.numel() + shift, dtype=t.dtype, device=t.device)
+        view = buf[shift:].view(t.shape)
+        view.copy_(t)
+        out[name] = view
+    return out
+
+
+def run_case(B, Hq, Hkv, N, d, kb, vb, ctx, seed, tag, k_mul=1.0, v_mul=1.0, q_mul=1.0, misalign=False):
+    _say(f"[gpu attn] {tag}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} k{kb}v{vb} ctx={list(ctx)[:8]}")
     k, v = synth.kv_inputs("normal", B, N, Hkv, d, seed)         # [B, N, Hkv, d]
     q = synth.queries(B, Hq, d, seed + 7)
+    k, v, q = _scaled(k, k_mul), _scaled(v, v_mul), _scaled(q, q_mul)
     signs = synth.sign_vector(d)
     sig = torch.from_numpy(signs).to(DEV)
     cache = tq.quantize_into_cache(k.to(DEV), v.to(DEV), sig, kb, vb)
+    if misalign:
+        cache = _misaligned(cache)
     ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
     out = tq.decode_attn(q.to(DEV), cache, ctx_t, sig, kb, vb, Hkv)
     torch.cuda.synchronize()
@@ -65,6 +85,28 @@ def test_head_groupings(Hq, Hkv):
                                      (64, 4, 2), (256, 8, 3)])
 def test_schemes(d, kb, vb):
     run_case(2, 8, 2, 257, d, kb, vb, [257, 100], 13, f"d{d} k{kb}v{vb}")
+
+
+@pytest.mark.parametrize("k_mul,v_mul,q_mul", [(1.0, 1e-4, 1.0), (1.0, 1e-6, 1.0), (1e-3, 1.0, 1e3),
+                                               (1e-5, 1.0, 2e5), (1.0, 1.0, 1e-3), (1.0, 300.0, 1.0)])
+def test_magnitudes(k_mul, v_mul, q_mul):
+    # tiny values, keys and queries of opposite extreme scales, near-uniform
+    # attention, large values: the fp16 operands must stay in range
+    run_case(2, 8, 2, 400, 128, 8, 3, [400, 233], 15, f"k*{k_mul} v*{v_mul} q*{q_mul}", k_mul, v_mul, q_mul)
+
+
+@pytest.mark.parametrize("d,vb", [(128, 3), (64, 2)])
+def test_misaligned_planes(d, vb):
+    # planes off the 16/4-byte alignment the DMA copies need: the other kernel serves them
+    run_case(2, 8, 2, 300, d, 8, vb, [300, 129], 16, f"misaligned d{d} v{vb}", misalign=True)
+
+
+def test_many_steps_ragged_tails():
+    # 1024 (sequence, kv-head) units -> two splits of 512 tokens, four 32-token
+    # steps per wave; the contexts end inside the first step, mid-split and
+    # one token short of the cache
+    ctx = [1000, 999, 517, 33]
+    run_case(4, 256, 256, 1000, 128, 8, 3, ctx, 17, "many steps ragged")
 
 
 def test_empty_context_gives_zero_rows():
