@@ -176,6 +176,109 @@ __device__ __forceinline__ void load_group(const uint16_t* p, uint32_t (&u)[16])
   }
 }
 
+// ------------------------------------------------------------ input tiles
+// A wave's rows for one iteration form one 4 KB tile: 64 lanes x one
+// 32-element group (64 bytes).  Loading it group by group leaves every load
+// instruction scattered over the tile (64 bytes apart per lane), which costs a
+// quarter of the achievable HBM rate; instead the tile is copied HBM -> LDS
+// by four global_load_lds_dwordx4 of 64 x 16 bytes, one iteration ahead of
+// its use, and each lane then reads its own group back from LDS.  Copy slot p
+// holds quarter q of reader lane L's group with p = 4L + ((q + L/2) mod 4):
+// every eight consecutive readers of a quarter hit distinct 16-byte bank
+// groups.  The copies are inline assembly so the compiler does not wait for
+// them before unrelated LDS reads; M0 (their LDS base) is reserved by the
+// compiler and read by no other instruction of these kernels.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef uint32_t tq_u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tq_u32x4 lds_u32x4;
+constexpr int kTile = 4096;
+
+__device__ __forceinline__ int tile_slot(int reader, int q) { return 4 * reader + ((q + (reader >> 1)) & 3); }
+
+__device__ __forceinline__ void tile_copy16(const void* src, const lds_u8* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"((uint32_t)(uintptr_t)dst)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Rows r of a tensor are memory rows r (no head, token or sequence gaps).
+__device__ __forceinline__ bool rows_contiguous(const RowMap& m, const RowSplit& sp) {
+  return m.head_stride == 1 && m.tok_stride == (int64_t)sp.div_head.d &&
+         m.seq_stride == (int64_t)sp.div_tok.d * sp.div_head.d;
+}
+
+// Byte offset, within a contiguous tile, of copy slot 64j + lane.
+template <int D>
+__device__ __forceinline__ uint32_t tile_src_offset(int j, int lane) {
+  using L = GroupLanes<D>;
+  const int p = 64 * j + lane, reader = p >> 2, q = ((p & 3) - (reader >> 1)) & 3;
+  return (uint32_t)(2 * (L::row(reader) * D + kGroup * L::group(reader) + 8 * q));
+}
+
+// Copies of a whole tile of contiguous rows: scalar base, lane offsets fixed.
+__device__ __forceinline__ void tile_issue_contig(const uint16_t* src, uint32_t base_row, int d,
+                                                  const uint32_t (&off)[4], const lds_u8* stage) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(src) + (uint64_t)base_row * (uint64_t)(2 * d);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off[j]), "s"(b),
+                 "s"((uint32_t)(uintptr_t)(stage + 1024 * j))
+                 : "memory", "m0");
+}
+
+// Issue the four copies of the tile of rows base .. base + RPW - 1 (rows past
+// the end re-read the last row; their results are never stored).
+template <int D>
+__device__ __forceinline__ void tile_issue(const uint16_t* src, const QuantArgs& a, uint32_t base, bool contig,
+                                           const uint32_t (&off)[4], const lds_u8* stage, int lane) {
+  using L = GroupLanes<D>;
+  if (contig && base + L::RPW <= a.rows) {
+    tile_issue_contig(src, base, D, off, stage);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 64 * j + lane, reader = p >> 2, q = ((p & 3) - (reader >> 1)) & 3;
+    uint32_t r = base + (uint32_t)L::row(reader);
+    if (r >= a.rows) r = a.rows - 1;
+    int64_t irow = r;
+    if (!contig) {
+      uint32_t s, t, h;
+      split_row(r, a.split, s, t, h);
+      irow = row_index(a.in, s, t, h);
+    }
+    tile_copy16(src + irow * D + kGroup * L::group(reader) + 8 * q, stage + 1024 * j);
+  }
+}
+
+__device__ __forceinline__ void tile_read(const lds_u8* stage, int lane, uint32_t (&u)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const tq_u32x4 w = *(const lds_u32x4*)(stage + 16 * tile_slot(lane, q));
+    u[4 * q] = w.x; u[4 * q + 1] = w.y; u[4 * q + 2] = w.z; u[4 * q + 3] = w.w;
+  }
+}
+
+// Wait until the tile of this iteration has landed.  Issued after it: the
+// previous iteration's stores (at least one instruction per output array,
+// `min_stores`) and, with `next`, the next tile's four copies.  vmcnt retires
+// in issue order, so allowing that many to remain outstanding is exact or
+// conservative.
+template <int MinStores>
+__device__ __forceinline__ void tile_wait(bool first, bool next) {
+  if (next) {
+    if (first) wait_vmcnt<4>();
+    else wait_vmcnt<4 + MinStores>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // Exact division of every element by a per-group divisor s: with r = RN(1/s),
 // q0 = RN(y r), e = y - q0 s (exact by fma), q = RN(q0 + e r) equals RN(y/s)
 // (Markstein 1990) while s is a normal number and no step overflows.
@@ -221,22 +324,34 @@ __device__ __forceinline__ uint32_t lloyd_max_index(float yn, const float* lds_b
 
 // ------------------------------------------------------------------ keys
 template <int D, int KB>
-__device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t blk, uint32_t nblk) {
+__device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t blk, uint32_t nblk, uint8_t* tile_lds) {
   using L = GroupLanes<D>;
   constexpr int G = D / kGroup;
   const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
-  const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
-  const uint32_t nwave = nblk * 4u;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wave = blk * 4u + (uint32_t)wv;
+  const uint32_t nwave = nblk * 4u, stride = nwave * L::RPW;
   const float lo = KB == 8 ? -127.f : 0.f;
   const float hi = KB == 8 ? 127.f : (float)((1 << KB) - 1);
-  for (uint32_t base = wave * L::RPW; base < a.rows; base += nwave * L::RPW) {
-    const uint32_t r = base + rw;
-    if (r >= a.rows) continue;
-    uint32_t s, t, h;
-    split_row(r, a.split, s, t, h);
-    const int64_t irow = row_index(a.in, s, t, h), orow = row_index(a.out, s, t, h);
+  const lds_u8* const tiles = (const lds_u8*)(tile_lds + wv * 2 * kTile);
+  const bool contig = rows_contiguous(a.in, a.split), contig_out = rows_contiguous(a.out, a.split);
+  const uint32_t off[4] = {tile_src_offset<D>(0, lane), tile_src_offset<D>(1, lane), tile_src_offset<D>(2, lane),
+                           tile_src_offset<D>(3, lane)};
+  uint32_t base = wave * L::RPW;
+  if (base < a.rows) tile_issue<D>(a.k, a, base, contig, off, tiles, lane);
+  for (int it = 0; base < a.rows; base += stride, ++it) {
+    const bool next = base + stride < a.rows;
+    if (next) tile_issue<D>(a.k, a, base + stride, contig, off, tiles + ((it + 1) & 1) * kTile, lane);
+    tile_wait<3>(it == 0, next);  // k_q, k_scale, k_zero stores
     uint32_t u[16];
-    load_group(a.k + irow * D + kGroup * g, u);
+    tile_read(tiles + (it & 1) * kTile, lane, u);
+    const uint32_t r = base + rw;
+    int64_t orow = r;
+    if (!contig_out) {
+      uint32_t s, t, h;
+      split_row(r < a.rows ? r : 0u, a.split, s, t, h);
+      orow = row_index(a.out, s, t, h);
+    }
     float x[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -284,9 +399,11 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
         o[i] = lo2 | hi2;
       }
       // the key plane is only 8-byte aligned: four 8-byte stores
-      uint2* dst = reinterpret_cast<uint2*>(a.k_q + orow * D + kGroup * g);
+      if (r < a.rows) {
+        uint2* dst = reinterpret_cast<uint2*>(a.k_q + orow * D + kGroup * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = make_uint2(o[2 * i], o[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) dst[i] = make_uint2(o[2 * i], o[2 * i + 1]);
+      }
     } else {
       uint32_t o[KB] = {};
 #pragma unroll
@@ -296,18 +413,23 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
         o[wd] |= v << off;
         if (off + KB > 32) o[wd + 1] |= v >> (32 - off);
       }
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_q + orow * (D * KB / 8) + 4 * KB * g);
+      if (r < a.rows) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_q + orow * (D * KB / 8) + 4 * KB * g);
 #pragma unroll
-      for (int i = 0; i < KB; ++i) dst[i] = o[i];
+        for (int i = 0; i < KB; ++i) dst[i] = o[i];
+      }
     }
-    a.k_scale[orow * G + g] = (uint16_t)f16_bits(scale);
-    a.k_zero[orow * G + g] = (uint16_t)f16_bits(zero);
+    if (r < a.rows) {
+      a.k_scale[orow * G + g] = (uint16_t)f16_bits(scale);
+      a.k_zero[orow * G + g] = (uint16_t)f16_bits(zero);
+    }
   }
 }
 
 // ---------------------------------------------------------------- values
 template <int D, int VB>
-__device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_t blk, uint32_t nblk) {
+__device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_t blk, uint32_t nblk,
+                                                     uint8_t* tile_lds) {
   using L = GroupLanes<D>;
   constexpr int G = D / kGroup;
   __shared__ float bnd_lds[VB >= 5 ? (1 << VB) : 1];
@@ -317,8 +439,9 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
     __syncthreads();
   }
   const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
-  const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
-  const uint32_t nwave = nblk * 4u;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wave = blk * 4u + (uint32_t)wv;
+  const uint32_t nwave = nblk * 4u, stride = nwave * L::RPW;
   // sign masks of this lane's 32 elements, two per bf16 pair (bits 15 and 31)
   uint32_t smask[16];
   {
@@ -332,19 +455,26 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
     }
   }
   const float rd = inv_sqrt_d<D>();
-  for (uint32_t base = wave * L::RPW; base < a.rows; base += nwave * L::RPW) {
+  const lds_u8* const tiles = (const lds_u8*)(tile_lds + wv * 2 * kTile);
+  const bool contig = rows_contiguous(a.in, a.split), contig_out = rows_contiguous(a.out, a.split);
+  const uint32_t off[4] = {tile_src_offset<D>(0, lane), tile_src_offset<D>(1, lane), tile_src_offset<D>(2, lane),
+                           tile_src_offset<D>(3, lane)};
+  uint32_t base = wave * L::RPW;
+  if (base < a.rows) tile_issue<D>(a.v, a, base, contig, off, tiles, lane);
+  for (int it = 0; base < a.rows; base += stride, ++it) {
+    const bool next = base + stride < a.rows;
+    if (next) tile_issue<D>(a.v, a, base + stride, contig, off, tiles + ((it + 1) & 1) * kTile, lane);
+    tile_wait<2>(it == 0, next);  // v_q, v_scale stores
     const uint32_t r = base + rw;
     const bool active = r < a.rows;
-    uint32_t s, t, h;
-    split_row(active ? r : 0u, a.split, s, t, h);
-    const int64_t irow = row_index(a.in, s, t, h), orow = row_index(a.out, s, t, h);
-    uint32_t u[16];
-    if (active) {
-      load_group(a.v + irow * D + kGroup * g, u);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) u[i] = 0;
+    int64_t orow = r;
+    if (!contig_out) {
+      uint32_t s, t, h;
+      split_row(active ? r : 0u, a.split, s, t, h);
+      orow = row_index(a.out, s, t, h);
     }
+    uint32_t u[16];
+    tile_read(tiles + (it & 1) * kTile, lane, u);
     float w[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -367,21 +497,50 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
     const float scale = __builtin_sqrtf(e[0] * 0.03125f);
     const float den = scale + 1e-8f;
     const bool fast = normal_divisor(den);
-    const float rcp = 1.0f / den;
-    if (fast) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) y[i] = div_markstein(y[i], den, rcp);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) y[i] = y[i] / den;
-    }
     uint32_t o[VB] = {};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t idx = lloyd_max_index<VB>(y[i], bnd_lds);
+    auto put = [&](int i, uint32_t idx) {
       const int bit = VB * i, wd = bit >> 5, off = bit & 31;
       o[wd] |= idx << off;
       if (off + VB > 32) o[wd + 1] |= idx >> (32 - off);
+    };
+    if (VB <= 4 && fast) {
+      // Compare |y| itself against the group's thresholds RN(b * den) for the
+      // positive boundaries b instead of dividing every element.  The index
+      // can then differ from that of RN(y / den) only where y / den lies within
+      // a few ulps (< 5e-7) of a boundary -- exact equality included -- inside
+      // the tie window the format allows.  With c = #{thresholds below |y|},
+      // the index is H + 1 + c above zero and H - c otherwise.
+      constexpr int H = (1 << (VB - 1)) - 1;
+      const uint32_t* bnd = boundaries<VB>();
+      float thr[H > 0 ? H : 1];
+#pragma unroll
+      for (int j = 1; j <= H; ++j) thr[j - 1] = __uint_as_float(bnd[H + j]) * den;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float ay = __builtin_fabsf(y[i]);
+        uint32_t c;
+        if constexpr (H == 3) {
+          // two-level search: the middle threshold, then the outer one
+          const bool hi = ay > thr[1];
+          c = (hi ? 2u : 0u) + ((ay > (hi ? thr[2] : thr[0])) ? 1u : 0u);
+        } else {
+          c = 0;
+#pragma unroll
+          for (int j = 0; j < H; ++j) c += (ay > thr[j]) ? 1u : 0u;
+        }
+        put(i, c ^ ((y[i] > 0.f) ? (uint32_t)(H + 1) : (uint32_t)H));
+      }
+    } else {
+      const float rcp = 1.0f / den;
+      if (fast) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) y[i] = div_markstein(y[i], den, rcp);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) y[i] = y[i] / den;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) put(i, lloyd_max_index<VB>(y[i], bnd_lds));
     }
     if (active) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.v_q + orow * (D * VB / 8) + 4 * VB * g);
@@ -613,11 +772,13 @@ __device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uin
 // so both halves progress side by side over the whole grid.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+  // two input tiles per wave (the current one and the next one in flight)
+  __shared__ __attribute__((aligned(16))) uint8_t tile_lds[4 * 2 * kTile];
   const uint32_t blk = blockIdx.x >> 1, nblk = gridDim.x >> 1;
   if (blockIdx.x & 1)
-    quantize_values_rows<D, VB>(a, blk, nblk);
+    quantize_values_rows<D, VB>(a, blk, nblk, tile_lds);
   else
-    quantize_keys_rows<D, KB>(a, blk, nblk);
+    quantize_keys_rows<D, KB>(a, blk, nblk, tile_lds);
 }
 
 template <int D, int KB, int VB>
