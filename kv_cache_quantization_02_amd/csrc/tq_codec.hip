@@ -579,7 +579,12 @@ __device__ __forceinline__ void store_tile(const uint32_t (&o)[16], uint16_t* ba
     const int c = lane + 64 * j;
     const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_offset(c));
     const int64_t off = offs[c / CPR];
-    if (off >= 0) *reinterpret_cast<uint4*>(base + off + 8 * (c % CPR)) = v;
+    // streaming store: the bf16 output is not re-read by this kernel, so it
+    // should not displace other data from the caches
+    if (off >= 0) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(base + off + 8 * (c % CPR)));
+    }
   }
   __builtin_amdgcn_wave_barrier();
 }
