@@ -80,6 +80,59 @@ def cpu_baseline(k, v, signs, rows: int):
                       f"prefill chunk (k8v3, d128), numpy float32 on one host core, {dt:.1f} s"}
 
 
+def _time_us(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
+    """Timings of the cache append and windowed-fetch entry points, outside the
+    timed step: the decode-append workload (64 layers x 32 sequences x 8 kv-heads,
+    one new token each, one launch into a [2048, 8, 1024] cache at per-sequence
+    positions) and full-window fetches of the decode cache above."""
+    import torch
+    rec, L, T, H, dd, akb, avb, seed = synth.WORKLOADS["decode_append_k8v3_d128"]
+    k, v = synth.kv_inputs(rec, L, T, H, dd, seed, device=dev)
+    k, v = k.reshape(L * T, 1, H, dd), v.reshape(L * T, 1, H, dd)
+    cap = 1024
+    acache = tq.alloc_planes(tq.scheme(dd, akb, avb), (L * T, H, cap), dev)
+    pos = torch.randint(0, cap, (L * T,), generator=torch.Generator().manual_seed(seed),
+                        dtype=torch.int32).to(dev)
+    rows = L * T * H
+    us_a = _time_us(lambda: tq.append_kv(k, v, acache, pos, sig, akb, avb), 50)
+    row_bytes = tq.tq_row_bytes(tq.scheme(d, kb, vb))
+    lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+    kw = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
+    vw = torch.empty_like(kw)
+    planes = tq.planes_struct(cache)
+    sch = tq.scheme(d, kb, vb)
+
+    def fetch(rot):
+        st = tq.tq_fetch_kv(sch, planes, B, Hkv, Hkv * N, N, lens, N, sig, rot, kw, vw)
+        assert st == 0, st
+    us_e = _time_us(lambda: fetch(False), 10)
+    us_r = _time_us(lambda: fetch(True), 10)
+    fb = B * Hkv * N * (row_bytes + 4 * d)
+    del kw, vw, acache
+    return {
+        "append_kv": {"workload": f"decode append k{akb}v{avb} d{dd}: {L}x{T}x{H} rows, 1 token each, one launch",
+                      "us": us_a, "token_heads_per_s": rows / (us_a * 1e-6),
+                      "GBps": rows * (4 * dd + tq.tq_row_bytes(tq.scheme(dd, akb, avb))) / (us_a * 1e-6) / 1e9},
+        "fetch_kv_eager": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache",
+                           "us": us_e, "GBps": fb / (us_e * 1e-6) / 1e9},
+        "fetch_kv_rotated": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache, values rotated",
+                             "us": us_r, "GBps": fb / (us_r * 1e-6) / 1e9},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +140,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1048576)
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the separate timings of the cache append / windowed fetch entry points")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run plain 1 GiB device copies (untimed) so a "
                          "counter run can scale FETCH_SIZE/WRITE_SIZE by a kernel of known traffic")
@@ -182,6 +237,10 @@ def main():
                 "frac": phases[dom]["GBps"] / HBM_PEAK_GBS, "traffic": measured_traffic(kname),
                 "kernel": phases[dom]["kernel"], "algorithmic_bytes_per_launch": dom_bytes}
 
+    next_rows = None
+    if not args.no_next:
+        next_rows = measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev)
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -209,6 +268,7 @@ def main():
         "phases": phases,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "next_rows": next_rows,
     }
     print(json.dumps(line), flush=True)
 

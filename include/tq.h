@@ -136,6 +136,39 @@ int32_t tq_dequantize_kv(const tq_scheme* scheme, const tq_planes* in, const tq_
                          const int8_t* signs, uint16_t* k_bf16, uint16_t* v_bf16,
                          const tq_rows* out_rows, void* stream);
 
+/* Append new tokens into a [batch, kv-head, capacity] cache at per-sequence
+ * positions: only the appended tokens are quantized, the rest of the cache is
+ * untouched (TurboQuant page, "Architecture in mlx-bun": the cache's
+ * update quantizes just the newly appended tokens into packed storage).
+ *   k_bf16, v_bf16 : [batch, n_new, n_kv_heads, head_dim], contiguous
+ *   cache          : planes; row(b, g, t) = b*seq_stride_rows + g*head_stride_rows + t
+ *   positions      : device int32[batch]; token j of sequence b goes to cache
+ *                    token positions[b] + j, and is written only when
+ *                    0 <= positions[b] + j < capacity (others are dropped)
+ * Quantization is exactly that of tq_quantize_kv.  Returns TQ_OK or TQ_E_*. */
+int32_t tq_append_kv(const tq_scheme* scheme, const uint16_t* k_bf16, const uint16_t* v_bf16, int32_t batch,
+                     int32_t n_new, int32_t n_kv_heads, const int8_t* signs, const tq_planes* cache,
+                     int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* positions,
+                     int32_t capacity, void* stream);
+
+/* Fetch the active window of every (sequence, kv head) as bf16 (TurboQuant
+ * page, "Architecture in mlx-bun": the cache returns its dequantized bf16
+ * active window; "Deferred inverse FWHT": the V window may stay in the
+ * rotated domain so that attention un-rotates its output once).
+ *   cache          : planes addressed as in tq_append_kv
+ *   lens           : device int32[batch]; tokens t < lens[b] are live
+ *   window         : tokens per output row block (>= every lens[b] the caller
+ *                    wants whole); output rows t >= lens[b] are written as +0
+ *   values_rotated : 0 -> V as tq_dequantize_kv (signs needed);
+ *                    1 -> V rows are centroid[idx] * scale16 rounded to bf16,
+ *                    no transform and no signs (signs may be NULL)
+ *   k_bf16, v_bf16 : [batch, n_kv_heads, window, head_dim], either may be NULL
+ * Keys are always dequantized as in tq_dequantize_kv.  Returns TQ_OK or TQ_E_*. */
+int32_t tq_fetch_kv(const tq_scheme* scheme, const tq_planes* cache, int32_t batch, int32_t n_kv_heads,
+                    int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* lens, int32_t window,
+                    const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16, uint16_t* v_bf16,
+                    void* stream);
+
 /* Workspace bytes tq_decode_attn_quant needs for these sizes (host only);
  * 0 when the arguments are invalid. */
 size_t tq_decode_attn_workspace_bytes(const tq_scheme* scheme, int32_t batch, int32_t n_q_heads,

@@ -62,6 +62,14 @@ def lib() -> ctypes.CDLL:
         L.tq_dequantize_kv.argtypes = [P(Scheme), P(Planes), P(Rows), ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, P(Rows), ctypes.c_void_p]
         L.tq_dequantize_kv.restype = ctypes.c_int32
+        L.tq_append_kv.argtypes = [P(Scheme), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_void_p, P(Planes), ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        L.tq_append_kv.restype = ctypes.c_int32
+        L.tq_fetch_kv.argtypes = [P(Scheme), P(Planes), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.tq_fetch_kv.restype = ctypes.c_int32
         L.tq_decode_attn_workspace_bytes.argtypes = [P(Scheme), ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.c_int32]
         L.tq_decode_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -125,6 +133,20 @@ def tq_codebook(bits: int):
 def tq_quantize_kv(scheme, k, v, in_rows, signs, out, out_rows, stream=None) -> int:
     return lib().tq_quantize_kv(ctypes.byref(scheme), _ptr(k), _ptr(v), ctypes.byref(in_rows),
                                 _ptr(signs), ctypes.byref(out), ctypes.byref(out_rows), _stream(stream))
+
+
+def tq_append_kv(scheme, k, v, batch, n_new, n_kv_heads, signs, cache, seq_stride_rows, head_stride_rows,
+                 positions, capacity, stream=None) -> int:
+    return lib().tq_append_kv(ctypes.byref(scheme), _ptr(k), _ptr(v), batch, n_new, n_kv_heads, _ptr(signs),
+                              ctypes.byref(cache), seq_stride_rows, head_stride_rows, _ptr(positions),
+                              capacity, _stream(stream))
+
+
+def tq_fetch_kv(scheme, cache, batch, n_kv_heads, seq_stride_rows, head_stride_rows, lens, window, signs,
+                values_rotated, k_out, v_out, stream=None) -> int:
+    return lib().tq_fetch_kv(ctypes.byref(scheme), ctypes.byref(cache), batch, n_kv_heads, seq_stride_rows,
+                             head_stride_rows, _ptr(lens), window, _ptr(signs), int(values_rotated),
+                             _ptr(k_out), _ptr(v_out), _stream(stream))
 
 
 def tq_dequantize_kv(scheme, planes, in_rows, signs, k_out, v_out, out_rows, stream=None) -> int:
@@ -240,3 +262,27 @@ def decode_attn(q: torch.Tensor, cache: dict, ctx_lens: torch.Tensor, signs: tor
                                 ctx_lens, N, float(softmax_scale), signs, out, workspace,
                                 workspace.numel()), "tq_decode_attn_quant")
     return out
+
+
+def append_kv(k: torch.Tensor, v: torch.Tensor, cache: dict, positions: torch.Tensor, signs: torch.Tensor,
+              k_bits: int, v_bits: int) -> dict:
+    """Append bf16 [B, n_new, Hkv, d] tokens into a cache laid out [B, Hkv, capacity, bytes]
+    at device int32 positions [B]; tokens at or past the capacity are dropped."""
+    B, n_new, H, d = k.shape
+    cap = cache["k_q"].shape[2]
+    _check(tq_append_kv(scheme(d, k_bits, v_bits), k, v, B, n_new, H, signs, planes_struct(cache), H * cap, cap,
+                        positions, cap), "tq_append_kv")
+    return cache
+
+
+def fetch_kv(cache: dict, lens: torch.Tensor, window: int, signs: torch.Tensor | None, head_dim: int,
+             k_bits: int, v_bits: int, values_rotated: bool = False, keys: bool = True, values: bool = True):
+    """bf16 [B, Hkv, window, d] K and V of a [B, Hkv, capacity, bytes] cache; rows t >= lens[b] are +0.
+    With values_rotated the V rows stay in the rotated domain (centroid * scale)."""
+    B, H, cap = cache["k_q"].shape[:3]
+    dev = cache["k_q"].device
+    k_out = torch.empty((B, H, window, head_dim), dtype=torch.bfloat16, device=dev) if keys else None
+    v_out = torch.empty((B, H, window, head_dim), dtype=torch.bfloat16, device=dev) if values else None
+    _check(tq_fetch_kv(scheme(head_dim, k_bits, v_bits), planes_struct(cache), B, H, H * cap, cap, lens, window,
+                       signs, values_rotated, k_out, v_out), "tq_fetch_kv")
+    return k_out, v_out

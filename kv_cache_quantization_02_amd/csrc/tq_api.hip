@@ -185,6 +185,84 @@ int32_t tq_dequantize_kv(const tq_scheme* s, const tq_planes* in, const tq_rows*
                                           kMaxCodecBlocks));
 }
 
+int32_t tq_append_kv(const tq_scheme* s, const uint16_t* k_bf16, const uint16_t* v_bf16, int32_t batch,
+                     int32_t n_new, int32_t n_kv_heads, const int8_t* signs, const tq_planes* cache,
+                     int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* positions,
+                     int32_t capacity, void* stream) {
+  int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  if (!k_bf16 || !v_bf16 || !signs || !positions) return TQ_E_NULL;
+  if ((st = check_planes(cache)) != TQ_OK) return st;
+  if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(signs)) return TQ_E_ALIGN;
+  if (batch < 0 || n_new < 0 || n_kv_heads < 0 || capacity < 0 || seq_stride_rows < 0 || head_stride_rows < 0)
+    return TQ_E_SHAPE;
+  // new tokens arrive as a contiguous [batch, n_new, n_kv_heads, d] block
+  const tq_rows in{batch, n_new, n_kv_heads, (int64_t)n_new * n_kv_heads, n_kv_heads, 1};
+  const tq_rows out{batch, n_new, n_kv_heads, seq_stride_rows, 1, head_stride_rows};
+  tq::QuantArgs a{};
+  tq::RowSplit split{};
+  uint32_t rows = 0;
+  if ((st = check_rows(&in, &rows, &split)) != TQ_OK) return st;
+  if (rows == 0 || capacity == 0) return TQ_OK;
+  a.k = k_bf16;
+  a.v = v_bf16;
+  a.signs = signs;
+  a.k_q = (uint8_t*)cache->k_q;
+  a.k_scale = (uint16_t*)cache->k_scale;
+  a.k_zero = (uint16_t*)cache->k_zero;
+  a.v_q = (uint8_t*)cache->v_q;
+  a.v_scale = (uint16_t*)cache->v_scale;
+  a.rows = rows;
+  a.split = split;
+  a.in = map_of(&in);
+  a.out = map_of(&out);
+  a.out_pos = positions;
+  a.out_cap = capacity;
+  return hip_status(tq::launch_quantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
+                                        kMaxCodecBlocks));
+}
+
+int32_t tq_fetch_kv(const tq_scheme* s, const tq_planes* cache, int32_t batch, int32_t n_kv_heads,
+                    int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* lens, int32_t window,
+                    const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16, uint16_t* v_bf16,
+                    void* stream) {
+  int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  if ((st = check_planes(cache)) != TQ_OK) return st;
+  if (!lens || (!k_bf16 && !v_bf16)) return TQ_E_NULL;
+  if (v_bf16 && !values_rotated && !signs) return TQ_E_NULL;
+  if ((k_bf16 && !aligned16(k_bf16)) || (v_bf16 && !aligned16(v_bf16)) || (signs && !aligned16(signs)))
+    return TQ_E_ALIGN;
+  if (batch < 0 || n_kv_heads < 0 || window < 0 || seq_stride_rows < 0 || head_stride_rows < 0)
+    return TQ_E_SHAPE;
+  // rows (b, g, t) of the cache window -> a contiguous [batch, n_kv_heads, window, d]
+  // output; the token is the fastest index, so a wave's rows are consecutive
+  // tokens of one kv head on both sides
+  const tq_rows in{batch, n_kv_heads, window, seq_stride_rows, head_stride_rows, 1};
+  const tq_rows out{batch, n_kv_heads, window, (int64_t)n_kv_heads * window, window, 1};
+  tq::DequantArgs a{};
+  tq::RowSplit split{};
+  uint32_t rows = 0;
+  if ((st = check_rows(&in, &rows, &split)) != TQ_OK) return st;
+  if (rows == 0) return TQ_OK;
+  a.k_q = (const uint8_t*)cache->k_q;
+  a.k_scale = (const uint16_t*)cache->k_scale;
+  a.k_zero = (const uint16_t*)cache->k_zero;
+  a.v_q = (const uint8_t*)cache->v_q;
+  a.v_scale = (const uint16_t*)cache->v_scale;
+  a.signs = signs;
+  a.k = k_bf16;
+  a.v = v_bf16;
+  a.rows = rows;
+  a.split = split;
+  a.in = map_of(&in);
+  a.out = map_of(&out);
+  a.in_len = lens;
+  a.rotated = values_rotated ? 1 : 0;
+  return hip_status(tq::launch_dequantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
+                                          kMaxCodecBlocks));
+}
+
 size_t tq_decode_attn_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t max_ctx) {
   if (check_scheme(s) != TQ_OK) return 0;

@@ -212,6 +212,22 @@ __device__ __forceinline__ bool rows_contiguous(const RowMap& m, const RowSplit&
          m.seq_stride == (int64_t)sp.div_tok.d * sp.div_head.d;
 }
 
+// Output row of input row r for the quantize kernels, or -1 when the row is
+// past the end or falls outside the cache window of an append.
+__device__ __forceinline__ int64_t quant_out_row(const QuantArgs& a, uint32_t r, bool contig_out) {
+  if (r >= a.rows) return -1;
+  if (contig_out) return r;
+  uint32_t s, t, h;
+  split_row(r, a.split, s, t, h);
+  int64_t o = row_index(a.out, s, t, h);
+  if (a.out_pos) {
+    const int64_t p = a.out_pos[s];
+    if (p + t < 0 || p + t >= a.out_cap) return -1;
+    o += p * a.out.tok_stride;
+  }
+  return o;
+}
+
 // Byte offset, within a contiguous tile, of copy slot 64j + lane.
 template <int D>
 __device__ __forceinline__ uint32_t tile_src_offset(int j, int lane) {
@@ -334,7 +350,8 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
   const float lo = KB == 8 ? -127.f : 0.f;
   const float hi = KB == 8 ? 127.f : (float)((1 << KB) - 1);
   const lds_u8* const tiles = (const lds_u8*)(tile_lds + wv * 2 * kTile);
-  const bool contig = rows_contiguous(a.in, a.split), contig_out = rows_contiguous(a.out, a.split);
+  const bool contig = rows_contiguous(a.in, a.split);
+  const bool contig_out = rows_contiguous(a.out, a.split) && !a.out_pos;
   const uint32_t off[4] = {tile_src_offset<D>(0, lane), tile_src_offset<D>(1, lane), tile_src_offset<D>(2, lane),
                            tile_src_offset<D>(3, lane)};
   uint32_t base = wave * L::RPW;
@@ -345,13 +362,8 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
     tile_wait<3>(it == 0, next);  // k_q, k_scale, k_zero stores
     uint32_t u[16];
     tile_read(tiles + (it & 1) * kTile, lane, u);
-    const uint32_t r = base + rw;
-    int64_t orow = r;
-    if (!contig_out) {
-      uint32_t s, t, h;
-      split_row(r < a.rows ? r : 0u, a.split, s, t, h);
-      orow = row_index(a.out, s, t, h);
-    }
+    const int64_t orow = quant_out_row(a, base + rw, contig_out);
+    const bool wr = orow >= 0;
     float x[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -399,7 +411,7 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
         o[i] = lo2 | hi2;
       }
       // the key plane is only 8-byte aligned: four 8-byte stores
-      if (r < a.rows) {
+      if (wr) {
         uint2* dst = reinterpret_cast<uint2*>(a.k_q + orow * D + kGroup * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = make_uint2(o[2 * i], o[2 * i + 1]);
@@ -413,13 +425,13 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
         o[wd] |= v << off;
         if (off + KB > 32) o[wd + 1] |= v >> (32 - off);
       }
-      if (r < a.rows) {
+      if (wr) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_q + orow * (D * KB / 8) + 4 * KB * g);
 #pragma unroll
         for (int i = 0; i < KB; ++i) dst[i] = o[i];
       }
     }
-    if (r < a.rows) {
+    if (wr) {
       a.k_scale[orow * G + g] = (uint16_t)f16_bits(scale);
       a.k_zero[orow * G + g] = (uint16_t)f16_bits(zero);
     }
@@ -456,7 +468,8 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
   }
   const float rd = inv_sqrt_d<D>();
   const lds_u8* const tiles = (const lds_u8*)(tile_lds + wv * 2 * kTile);
-  const bool contig = rows_contiguous(a.in, a.split), contig_out = rows_contiguous(a.out, a.split);
+  const bool contig = rows_contiguous(a.in, a.split);
+  const bool contig_out = rows_contiguous(a.out, a.split) && !a.out_pos;
   const uint32_t off[4] = {tile_src_offset<D>(0, lane), tile_src_offset<D>(1, lane), tile_src_offset<D>(2, lane),
                            tile_src_offset<D>(3, lane)};
   uint32_t base = wave * L::RPW;
@@ -465,14 +478,8 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
     const bool next = base + stride < a.rows;
     if (next) tile_issue<D>(a.v, a, base + stride, contig, off, tiles + ((it + 1) & 1) * kTile, lane);
     tile_wait<2>(it == 0, next);  // v_q, v_scale stores
-    const uint32_t r = base + rw;
-    const bool active = r < a.rows;
-    int64_t orow = r;
-    if (!contig_out) {
-      uint32_t s, t, h;
-      split_row(active ? r : 0u, a.split, s, t, h);
-      orow = row_index(a.out, s, t, h);
-    }
+    const int64_t orow = quant_out_row(a, base + rw, contig_out);
+    const bool active = orow >= 0;
     uint32_t u[16];
     tile_read(tiles + (it & 1) * kTile, lane, u);
     float w[32];
@@ -610,7 +617,7 @@ __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint3
     uint32_t wv[kBatch][KW];
     float sc[kBatch], zp[kBatch];
     int64_t orow[kBatch];
-    bool act[kBatch];
+    bool act[kBatch], live[kBatch];
     static_for<kBatch>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       const uint32_t r = base + u * step + rw;
@@ -619,9 +626,11 @@ __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint3
       split_row(act[u] ? r : 0u, a.split, s, t, h);
       const int64_t irow = row_index(a.in, s, t, h);
       orow[u] = row_index(a.out, s, t, h);
+      // tokens past a fetch window are not read and come out as +0
+      live[u] = act[u] && (!a.in_len || (int64_t)h < (int64_t)a.in_len[s]);
 #pragma unroll
       for (int i = 0; i < KW; ++i) wv[u][i] = 0;
-      if (act[u]) {
+      if (live[u]) {
         if constexpr (KB == 8) {
           const uint2* src = reinterpret_cast<const uint2*>(a.k_q + irow * D + kGroup * g);
 #pragma unroll
@@ -643,7 +652,7 @@ __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint3
       constexpr int u = decltype(uc)::value;
       // every lane takes part in the tile exchange; rows past the end compute
       // on zeros and are not stored
-      const float s16 = act[u] ? canon_nan(sc[u]) : 0.f, z16 = act[u] ? canon_nan(zp[u]) : 0.f;
+      const float s16 = live[u] ? canon_nan(sc[u]) : 0.f, z16 = live[u] ? canon_nan(zp[u]) : 0.f;
       float k[32];
       if constexpr (KB == 8) {
         // idx + zero == (idx + 128) + (zero - 128) exactly: both are integers
@@ -677,11 +686,13 @@ __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint3
 // One value group back to bf16: centroid lookup, scale, transform,
 // 1/sqrt(d), signs (applied to the rounded bf16 pair: an exact sign flip).
 // CANON rewrites NaN halves to 0x7FC0 after the sign flip.
+// With `rotated` the row stays in the rotated domain (centroid * scale, no
+// transform, no signs); rows with `zero` are written as +0.
 template <int D, int VB, bool CANON>
 __device__ __forceinline__ void dequant_value_group(const uint32_t (&wv)[VB], float sc, const float* cen,
                                                     const uint32_t (&smask)[16], float rd, int lane,
                                                     int g, int rw, uint16_t* base, int64_t off,
-                                                    uint8_t* tile, int64_t* offs) {
+                                                    uint8_t* tile, int64_t* offs, bool rotated, bool zero) {
   float z[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -693,10 +704,19 @@ __device__ __forceinline__ void dequant_value_group(const uint32_t (&wv)[VB], fl
       v = (wv[wd] >> off) | ((wv[wd + 1] << (32 - off)) & ((1u << VB) - 1));
     z[i] = cen[v] * sc;
   }
-  const float m = fwht_group<D>(z, lane) * rd;
   uint32_t o[16];
+  if (rotated) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = pack_bf16x2(z[2 * i] * m, z[2 * i + 1] * m) ^ smask[i];
+    for (int i = 0; i < 16; ++i) o[i] = pack_bf16x2(z[2 * i], z[2 * i + 1]);
+  } else {
+    const float m = fwht_group<D>(z, lane) * rd;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = pack_bf16x2(z[2 * i] * m, z[2 * i + 1] * m) ^ smask[i];
+  }
+  if (__any(zero)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = zero ? 0u : o[i];
+  }
   if constexpr (CANON) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -738,7 +758,7 @@ __device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uin
     uint32_t wv[kBatch][VB];
     float scb[kBatch];
     int64_t orow[kBatch];
-    bool act[kBatch];
+    bool act[kBatch], live[kBatch];
     static_for<kBatch>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       const uint32_t r = base + u * step + rw;
@@ -747,10 +767,11 @@ __device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uin
       split_row(act[u] ? r : 0u, a.split, s, t, h);
       const int64_t irow = row_index(a.in, s, t, h);
       orow[u] = row_index(a.out, s, t, h);
+      live[u] = act[u] && (!a.in_len || (int64_t)h < (int64_t)a.in_len[s]);
       scb[u] = 0.f;
 #pragma unroll
       for (int i = 0; i < VB; ++i) wv[u][i] = 0;
-      if (act[u]) {
+      if (live[u]) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(a.v_q + irow * (D * VB / 8) + 4 * VB * g);
 #pragma unroll
         for (int i = 0; i < VB; ++i) wv[u][i] = src[i];
@@ -763,12 +784,13 @@ __device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uin
       // zeros and skip the store.  Only a non-finite scale can produce NaN;
       // such rows take the variant that keeps every NaN at 0x7FC0.
       const float sc = canon_nan(scb[u]);
+      const bool rot = a.rotated != 0, zero = act[u] && !live[u];
       if (__any(!__builtin_isfinite(sc)))
         dequant_value_group<D, VB, true>(wv[u], sc, cen_lds, smask, rd, lane, g, rw, a.v,
-                                         act[u] ? orow[u] * D : -1, tile, offs);
+                                         act[u] ? orow[u] * D : -1, tile, offs, rot, zero);
       else
         dequant_value_group<D, VB, false>(wv[u], sc, cen_lds, smask, rd, lane, g, rw, a.v,
-                                          act[u] ? orow[u] * D : -1, tile, offs);
+                                          act[u] ? orow[u] * D : -1, tile, offs, rot, zero);
     });
   }
 }

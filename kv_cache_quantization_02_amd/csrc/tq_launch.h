@@ -27,6 +27,10 @@ struct QuantArgs {
   uint32_t rows;
   RowSplit split;
   RowMap in, out;
+  // Append into a cache: when out_pos is set, row (s, t, h) is written to
+  // out-row (s, out_pos[s] + t, h), and only when 0 <= out_pos[s] + t < out_cap.
+  const int32_t* out_pos;
+  int32_t out_cap;
 };
 
 struct DequantArgs {
@@ -41,6 +45,12 @@ struct DequantArgs {
   uint32_t rows;
   RowSplit split;
   RowMap in, out;
+  // Windowed fetch: when in_len is set, rows (s, t, h) with h >= in_len[s]
+  // are not read and are written as +0 (the fetch puts the token index last,
+  // so that consecutive rows are consecutive tokens of one kv head).
+  const int32_t* in_len;
+  // Values left in the rotated domain: centroid * scale16, no transform or signs.
+  int32_t rotated;
 };
 
 struct AttnArgs {

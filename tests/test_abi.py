@@ -126,6 +126,37 @@ def test_decode_attn_validation_errors_without_gpu():
     assert call(batch=0) == 0
 
 
+def test_append_validation_errors_without_gpu():
+    s = tq.scheme(128, 8, 3)
+    args = dict(k=FAKE, v=FAKE, batch=4, n_new=1, n_kv_heads=8, signs=FAKE, cache=_planes(),
+                seq_stride_rows=8 * 512, head_stride_rows=512, positions=FAKE, capacity=512)
+    call = lambda **kw: tq.tq_append_kv(s, **{**args, **kw})
+    assert tq.tq_append_kv(tq.scheme(128, 3, 3), **args) == -2
+    assert call(positions=None) == -3
+    assert call(signs=None) == -3
+    assert call(k=FAKE + 8) == -5
+    assert call(cache=tq.Planes(FAKE, FAKE, FAKE, FAKE + 4, FAKE)) == -5
+    assert call(n_new=-1) == -4
+    assert call(capacity=-1) == -4
+    assert call(head_stride_rows=-512) == -4
+    assert call(batch=0) == 0           # no rows: no-op
+    assert call(capacity=0) == 0        # nothing fits: no-op
+
+
+def test_fetch_validation_errors_without_gpu():
+    s = tq.scheme(128, 8, 3)
+    args = dict(cache=_planes(), batch=4, n_kv_heads=8, seq_stride_rows=8 * 512, head_stride_rows=512,
+                lens=FAKE, window=512, signs=FAKE, values_rotated=0, k_out=FAKE, v_out=FAKE)
+    call = lambda **kw: tq.tq_fetch_kv(s, **{**args, **kw})
+    assert call(lens=None) == -3
+    assert call(k_out=None, v_out=None) == -3
+    assert call(signs=None) == -3                       # eager values need the signs
+    assert call(v_out=FAKE + 2) == -5
+    assert call(window=-1) == -4
+    assert call(window=0) == 0          # empty window: no-op
+    assert tq.tq_fetch_kv(tq.scheme(100, 8, 3), **args) == -1
+
+
 def test_status_strings():
     assert tq.status_string(0) == "ok"
     assert "head_dim" in tq.status_string(-1)

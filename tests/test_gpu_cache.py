@@ -1,0 +1,150 @@
+"""GPU parity of tq_append_kv and tq_fetch_kv against oracle/cache.py.
+
+Append: the rows written must match the oracle's quantization of the new
+tokens (indices exact up to counted boundary ties, fp16 planes bit-exact) and
+every other cache row must keep its bytes.  Fetch: the planes are the
+oracle's own, so the bf16 windows must match the oracle bit for bit
+(eager and rotated values, +0 tails).
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_02_amd import binding as tq
+from kv_cache_quantization_02_amd import synth
+from oracle import cache as oc
+from oracle import codec
+from parity import compare_planes
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _np_planes(c):
+    return {n: (c[n].cpu().numpy() if n in ("k_q", "v_q") else c[n].cpu().numpy().view(np.uint16)) for n in tq.PLANES}
+
+
+def _to_gpu(c):
+    return {n: (torch.from_numpy(np.ascontiguousarray(c[n])).to(DEV) if n in ("k_q", "v_q") else
+                torch.from_numpy(np.ascontiguousarray(c[n]).view(np.float16)).to(DEV)) for n in tq.PLANES}
+
+
+def _sentinel_cache(B, H, cap, d, kb, vb, seed):
+    rng = np.random.default_rng(seed)
+    rb = codec.plane_row_bytes(d, kb, vb)
+    c = {}
+    for n in tq.PLANES:
+        if n in ("k_q", "v_q"):
+            c[n] = rng.integers(0, 256, (B, H, cap, rb[n]), dtype=np.uint8)
+        else:
+            c[n] = rng.integers(0, 0x3C00, (B, H, cap, rb[n] // 2), dtype=np.uint16)
+    return c
+
+
+@pytest.mark.parametrize("d,kb,vb", [(128, 8, 3), (256, 4, 4), (512, 5, 2), (64, 2, 5), (128, 8, 8)])
+def test_append_parity(d, kb, vb):
+    B, n, H, cap = 4, 3, 2, 40
+    pos = [0, 17, 38, -1]      # one sequence runs past the capacity, one starts before token 0
+    _say(f"[gpu cache] append d={d} k{kb}v{vb} B={B} n={n} H={H} cap={cap} pos={pos}")
+    k, v = synth.kv_inputs("normal", B, n, H, d, 31)
+    signs = synth.sign_vector(d)
+    before = _sentinel_cache(B, H, cap, d, kb, vb, 32)
+    gc = _to_gpu(before)
+    tq.append_kv(k.to(DEV), v.to(DEV), gc, torch.tensor(pos, dtype=torch.int32, device=DEV),
+                 torch.from_numpy(signs).to(DEV), kb, vb)
+    torch.cuda.synchronize()
+    got = _np_planes(gc)
+    want = oc.append_kv(before, synth.bf16_bits(k), synth.bf16_bits(v), pos, signs, kb, vb)
+    written = np.zeros((B, cap), bool)
+    for b, p in enumerate(pos):
+        for j in range(n):
+            if 0 <= p + j < cap:
+                written[b, p + j] = True
+    # untouched rows keep their bytes
+    for name in tq.PLANES:
+        g, b0 = got[name].transpose(0, 2, 1, 3), before[name].transpose(0, 2, 1, 3)   # [B, cap, H, bytes]
+        assert np.array_equal(g[~written], b0[~written]), f"{name}: rows outside the append changed"
+    # written rows: the codec's parity bar against a fresh oracle quantization of those tokens
+    kr = np.concatenate([synth.bf16_bits(k[b, j]) for b, p in enumerate(pos) for j in range(n) if 0 <= p + j < cap])
+    vr = np.concatenate([synth.bf16_bits(v[b, j]) for b, p in enumerate(pos) for j in range(n) if 0 <= p + j < cap])
+    ref = codec.quantize_kv(kr.reshape(-1, d), vr.reshape(-1, d), signs, kb, vb)
+    rows = {name: np.concatenate([got[name][b, :, p + j] for b, p in enumerate(pos) for j in range(n)
+                                  if 0 <= p + j < cap]) for name in tq.PLANES}
+    st = compare_planes(rows, ref, d, kb, vb)
+    _say(f"[gpu cache] append d={d} k{kb}v{vb}: {st}")
+    # and the whole cache equals the oracle's wherever no tie was counted
+    if st["key_ties"] == 0 and st["value_ties"] == 0:
+        for name in tq.PLANES:
+            assert np.array_equal(got[name], want[name])
+
+
+@pytest.mark.parametrize("d,kb,vb", [(128, 8, 3), (256, 4, 4), (512, 5, 2), (64, 2, 5)])
+@pytest.mark.parametrize("rotated", [False, True])
+def test_fetch_parity(d, kb, vb, rotated):
+    B, H, cap = 4, 2, 33
+    lens, window = [33, 5, 0, 17], 33
+    _say(f"[gpu cache] fetch d={d} k{kb}v{vb} rotated={rotated} lens={lens} window={window}")
+    k, v = synth.kv_inputs("normal", B, cap, H, d, 33)
+    signs = synth.sign_vector(d)
+    empty = _sentinel_cache(B, H, cap, d, kb, vb, 34)
+    c = oc.append_kv(empty, synth.bf16_bits(k), synth.bf16_bits(v), [0] * B, signs, kb, vb)
+    gc = _to_gpu(c)
+    K, V = tq.fetch_kv(gc, torch.tensor(lens, dtype=torch.int32, device=DEV), window,
+                       torch.from_numpy(signs).to(DEV), d, kb, vb, values_rotated=rotated)
+    torch.cuda.synchronize()
+    Kr, Vr = oc.fetch_kv(c, lens, window, signs, d, kb, vb, values_rotated=rotated)
+    assert np.array_equal(synth.bf16_bits(K), Kr), "keys differ from the oracle"
+    assert np.array_equal(synth.bf16_bits(V), Vr), "values differ from the oracle"
+
+
+def test_fetch_short_window_and_single_outputs():
+    d, kb, vb = 128, 8, 3
+    B, H, cap = 2, 3, 50
+    lens, window = [50, 20], 24          # the window cuts the first sequence short
+    k, v = synth.kv_inputs("normal", B, cap, H, d, 35)
+    signs = synth.sign_vector(d)
+    c = oc.append_kv(_sentinel_cache(B, H, cap, d, kb, vb, 36), synth.bf16_bits(k), synth.bf16_bits(v),
+                     [0] * B, signs, kb, vb)
+    gc = _to_gpu(c)
+    L = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    sig = torch.from_numpy(signs).to(DEV)
+    K, _ = tq.fetch_kv(gc, L, window, sig, d, kb, vb, values=False)
+    _, V = tq.fetch_kv(gc, L, window, sig, d, kb, vb, keys=False)
+    torch.cuda.synchronize()
+    Kr, Vr = oc.fetch_kv(c, lens, window, signs, d, kb, vb)
+    assert np.array_equal(synth.bf16_bits(K), Kr)
+    assert np.array_equal(synth.bf16_bits(V), Vr)
+
+
+def test_decode_append_full_size_sampled():
+    # one token per sequence for 64 layers x 32 sequences x 8 kv-heads, appended in
+    # one launch into a [64*32, 8, capacity] cache at per-sequence positions
+    rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS["decode_append_k8v3_d128"]
+    cap = 512
+    _say(f"[gpu cache] full-size decode append: {L}x{T}x{H} rows, cap={cap}")
+    k, v = synth.kv_inputs(rec, L, T, H, d, seed, device=DEV)          # [L, T(=seqs), H, d]
+    k = k.reshape(L * T, 1, H, d)
+    v = v.reshape(L * T, 1, H, d)
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(0, cap, L * T).astype(np.int32)
+    signs = synth.sign_vector(d)
+    sch = tq.scheme(d, kb, vb)
+    gc = tq.alloc_planes(sch, (L * T, H, cap), DEV)
+    for n in tq.PLANES:
+        gc[n].zero_()
+    tq.append_kv(k, v, gc, torch.from_numpy(pos).to(DEV), torch.from_numpy(signs).to(DEV), kb, vb)
+    torch.cuda.synchronize()
+    got = _np_planes(gc)
+    for s in [0, 1, L * T // 2, L * T - 1]:
+        rows = {n: got[n][s, :, pos[s]] for n in tq.PLANES}
+        ref = codec.quantize_kv(synth.bf16_bits(k[s, 0]).reshape(H, d), synth.bf16_bits(v[s, 0]).reshape(H, d),
+                                signs, kb, vb)
+        compare_planes(rows, ref, d, kb, vb)
+        others = np.ones(cap, bool)
+        others[pos[s]] = False
+        for n in tq.PLANES:
+            assert not got[n][s, :, others].any()
