@@ -121,6 +121,13 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     us_e = _time_us(lambda: fetch(False), 10)
     us_r = _time_us(lambda: fetch(True), 10)
     fb = B * Hkv * N * (row_bytes + 4 * d)
+    # un-rotate the rotated V window back to the original domain (into the K buffer)
+    rws = tq.contiguous_rows((B * Hkv * N, 1, 1))
+
+    def unrot():
+        st = tq.tq_unrotate_rows(d, vw, rws, sig, kw, rws)
+        assert st == 0, st
+    us_u = _time_us(unrot, 10)
     del kw, vw, acache
     return {
         "append_kv": {"workload": f"decode append k{akb}v{avb} d{dd}: {L}x{T}x{H} rows, 1 token each, one launch",
@@ -130,6 +137,8 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
                            "us": us_e, "GBps": fb / (us_e * 1e-6) / 1e9},
         "fetch_kv_rotated": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache, values rotated",
                              "us": us_r, "GBps": fb / (us_r * 1e-6) / 1e9},
+        "unrotate_rows": {"workload": f"{B * Hkv * N} bf16 rows of d={d} (the rotated V window)",
+                          "us": us_u, "GBps": B * Hkv * N * 4 * d / (us_u * 1e-6) / 1e9},
     }
 
 

@@ -169,6 +169,21 @@ int32_t tq_fetch_kv(const tq_scheme* scheme, const tq_planes* cache, int32_t bat
                     const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16, uint16_t* v_bf16,
                     void* stream);
 
+/* Un-rotate bf16 rows: out = bf16(signs * FWHT(in) / sqrt(d)), the transform
+ * first and the signs last -- the inverse of the value rotation.  This is
+ * what an attention site that consumed a rotated V window (tq_fetch_kv with
+ * values_rotated) applies to its output rows, once per query row (TurboQuant
+ * page, "Deferred inverse FWHT").
+ *   in_bf16, out_bf16 : bf16 rows addressed by *in_rows / *out_rows (same
+ *                       counts); the same buffer and row map may be given
+ *                       for both (in place)
+ *   signs             : int8[head_dim] of +1/-1, the cache's sign vector
+ * Arithmetic is float32 in the butterfly order of the quantizer; NaN is
+ * written as 0x7FC0.  Returns TQ_OK, TQ_E_HEAD_DIM, TQ_E_NULL, TQ_E_ALIGN or
+ * TQ_E_SHAPE. */
+int32_t tq_unrotate_rows(int32_t head_dim, const uint16_t* in_bf16, const tq_rows* in_rows, const int8_t* signs,
+                         uint16_t* out_bf16, const tq_rows* out_rows, void* stream);
+
 /* Workspace bytes tq_decode_attn_quant needs for these sizes (host only);
  * 0 when the arguments are invalid. */
 size_t tq_decode_attn_workspace_bytes(const tq_scheme* scheme, int32_t batch, int32_t n_q_heads,

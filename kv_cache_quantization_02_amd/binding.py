@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.tq_fetch_kv.restype = ctypes.c_int32
+        L.tq_unrotate_rows.argtypes = [ctypes.c_int32, ctypes.c_void_p, P(Rows), ctypes.c_void_p, ctypes.c_void_p,
+                                       P(Rows), ctypes.c_void_p]
+        L.tq_unrotate_rows.restype = ctypes.c_int32
         L.tq_decode_attn_workspace_bytes.argtypes = [P(Scheme), ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.c_int32]
         L.tq_decode_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -147,6 +150,11 @@ def tq_fetch_kv(scheme, cache, batch, n_kv_heads, seq_stride_rows, head_stride_r
     return lib().tq_fetch_kv(ctypes.byref(scheme), ctypes.byref(cache), batch, n_kv_heads, seq_stride_rows,
                              head_stride_rows, _ptr(lens), window, _ptr(signs), int(values_rotated),
                              _ptr(k_out), _ptr(v_out), _stream(stream))
+
+
+def tq_unrotate_rows(head_dim, x, in_rows, signs, out, out_rows, stream=None) -> int:
+    return lib().tq_unrotate_rows(head_dim, _ptr(x), ctypes.byref(in_rows), _ptr(signs), _ptr(out),
+                                  ctypes.byref(out_rows), _stream(stream))
 
 
 def tq_dequantize_kv(scheme, planes, in_rows, signs, k_out, v_out, out_rows, stream=None) -> int:
@@ -286,3 +294,14 @@ def fetch_kv(cache: dict, lens: torch.Tensor, window: int, signs: torch.Tensor |
     _check(tq_fetch_kv(scheme(head_dim, k_bits, v_bits), planes_struct(cache), B, H, H * cap, cap, lens, window,
                        signs, values_rotated, k_out, v_out), "tq_fetch_kv")
     return k_out, v_out
+
+
+def unrotate_rows(x: torch.Tensor, signs: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [..., d] rows in the rotated domain -> signs * FWHT(x) / sqrt(d) (bf16); out may be x."""
+    d = x.shape[-1]
+    n = x.numel() // d
+    if out is None:
+        out = torch.empty_like(x)
+    r = contiguous_rows((n, 1, 1))
+    _check(tq_unrotate_rows(d, x, r, signs, out, r), "tq_unrotate_rows")
+    return out

@@ -263,6 +263,29 @@ int32_t tq_fetch_kv(const tq_scheme* s, const tq_planes* cache, int32_t batch, i
                                           kMaxCodecBlocks));
 }
 
+int32_t tq_unrotate_rows(int32_t head_dim, const uint16_t* in_bf16, const tq_rows* in_rows, const int8_t* signs,
+                         uint16_t* out_bf16, const tq_rows* out_rows, void* stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512) return TQ_E_HEAD_DIM;
+  if (!in_bf16 || !signs || !out_bf16) return TQ_E_NULL;
+  if (!aligned16(in_bf16) || !aligned16(signs) || !aligned16(out_bf16)) return TQ_E_ALIGN;
+  int32_t st;
+  tq::UnrotateArgs a{};
+  tq::RowSplit split{};
+  uint32_t rows = 0, rows_out = 0;
+  if ((st = check_rows(in_rows, &rows, &split)) != TQ_OK) return st;
+  if ((st = check_rows(out_rows, &rows_out, &split)) != TQ_OK) return st;
+  if (!same_counts(in_rows, out_rows)) return TQ_E_SHAPE;
+  if (rows == 0) return TQ_OK;
+  a.in = in_bf16;
+  a.signs = signs;
+  a.out = out_bf16;
+  a.rows = rows;
+  a.split = split;
+  a.in_map = map_of(in_rows);
+  a.out_map = map_of(out_rows);
+  return hip_status(tq::launch_unrotate(a, head_dim, (hipStream_t)stream, kMaxCodecBlocks));
+}
+
 size_t tq_decode_attn_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t max_ctx) {
   if (check_scheme(s) != TQ_OK) return 0;

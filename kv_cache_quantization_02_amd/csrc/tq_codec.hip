@@ -887,6 +887,80 @@ hipError_t launch_quantize(const QuantArgs& a, int d, int kb, int vb, hipStream_
   }
 }
 
+// ------------------------------------------------------ inverse rotation
+// bf16 rows in the rotated domain back to the original one:
+// out = signs * FWHT(in) / sqrt(d), the transform first and the signs last
+// (TurboQuant page, "Deferred inverse FWHT": the attention output is
+// un-rotated once per query row).  Same lane layout and tile stores as the
+// value dequantizer; every row is read before its tile is written, so the
+// call may work in place.
+template <int D>
+__global__ __launch_bounds__(256) void unrotate_kernel(UnrotateArgs a) {
+  using L = GroupLanes<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][kTileBytes];
+  __shared__ int64_t row_offs[4][L::RPW];
+  const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
+  uint8_t* tile = tiles[threadIdx.x >> 6];
+  int64_t* offs = row_offs[threadIdx.x >> 6];
+  const uint32_t wave = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const uint32_t step = gridDim.x * 4u * L::RPW;
+  uint32_t smask[16];
+  {
+    const uint4* sp = reinterpret_cast<const uint4*>(a.signs + kGroup * g);
+    const uint4 s0 = sp[0], s1 = sp[1];
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t word = sw[i >> 1] >> (16 * (i & 1));
+      smask[i] = ((word & 0x80u) << 8) | ((word & 0x8000u) << 16);
+    }
+  }
+  const float rd = inv_sqrt_d<D>();
+  for (uint32_t base = wave * L::RPW; base < a.rows; base += step) {
+    const uint32_t r = base + rw;
+    const bool act = r < a.rows;
+    uint32_t s, t, h;
+    split_row(act ? r : 0u, a.split, s, t, h);
+    const int64_t irow = row_index(a.in_map, s, t, h), orow = row_index(a.out_map, s, t, h);
+    uint32_t u[16];
+    if (act) {
+      load_group(a.in + irow * D + kGroup * g, u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = 0;
+    }
+    float w[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      w[2 * i] = bf16_lo(u[i]);
+      w[2 * i + 1] = bf16_hi(u[i]);
+    }
+    const float m = fwht_group<D>(w, lane) * rd;
+    uint32_t o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t p = pack_bf16x2(w[2 * i] * m, w[2 * i + 1] * m) ^ smask[i];
+      const uint32_t lo = p & 0xFFFFu, hi = p >> 16;
+      o[i] = (((lo & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : lo) | ((((hi & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : hi) << 16);
+    }
+    store_tile<D>(o, a.out, act ? orow * D : -1, tile, offs, lane, g, rw);
+  }
+}
+
+hipError_t launch_unrotate(const UnrotateArgs& a, int d, hipStream_t st, int max_blocks) {
+  const int rows_per_block = 4 * (64 / (d / kGroup));
+  long long blocks = ((long long)a.rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > max_blocks) blocks = max_blocks;
+  const dim3 grid((unsigned)blocks);
+  switch (d) {
+    case 64: unrotate_kernel<64><<<grid, 256, 0, st>>>(a); break;
+    case 128: unrotate_kernel<128><<<grid, 256, 0, st>>>(a); break;
+    case 256: unrotate_kernel<256><<<grid, 256, 0, st>>>(a); break;
+    default: unrotate_kernel<512><<<grid, 256, 0, st>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_dequantize(const DequantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks) {
   switch (d) {
     case 64: return launch_dequant_d<64>(a, kb, vb, st, max_blocks);

@@ -69,7 +69,18 @@ struct AttnArgs {
   float softmax_scale;
 };
 
+// Inverse rotation of bf16 rows: out = bf16(signs * FWHT(in) / sqrt(d)).
+struct UnrotateArgs {
+  const uint16_t* in;
+  const int8_t* signs;
+  uint16_t* out;
+  uint32_t rows;
+  RowSplit split;
+  RowMap in_map, out_map;
+};
+
 hipError_t launch_quantize(const QuantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
+hipError_t launch_unrotate(const UnrotateArgs& a, int d, hipStream_t st, int max_blocks);
 hipError_t launch_dequantize(const DequantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
 hipError_t launch_decode_attn(const AttnArgs& a, int d, int kb, int vb, hipStream_t st);
 

@@ -161,3 +161,14 @@ def test_status_strings():
     assert tq.status_string(0) == "ok"
     assert "head_dim" in tq.status_string(-1)
     assert tq.status_string(-99) == "unknown status"
+
+
+def test_unrotate_validation_errors_without_gpu():
+    r = tq.Rows(1, 4, 2, 8, 2, 1)
+    assert tq.tq_unrotate_rows(96, FAKE, r, FAKE, FAKE, r) == -1
+    assert tq.tq_unrotate_rows(128, None, r, FAKE, FAKE, r) == -3
+    assert tq.tq_unrotate_rows(128, FAKE, r, None, FAKE, r) == -3
+    assert tq.tq_unrotate_rows(128, FAKE + 2, r, FAKE, FAKE, r) == -5
+    assert tq.tq_unrotate_rows(128, FAKE, r, FAKE, FAKE, tq.Rows(1, 4, 3, 12, 3, 1)) == -4
+    z = tq.Rows(0, 4, 2, 8, 2, 1)
+    assert tq.tq_unrotate_rows(128, FAKE, z, FAKE, FAKE, z) == 0
