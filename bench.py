@@ -129,6 +129,25 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
         assert st == 0, st
     us_u = _time_us(unrot, 10)
     del kw, vw, acache
+    # multi-query (speculative, 4 query tokens per sequence) over the same cache
+    M = 4
+    qm = synth.queries(B * M, 32, d, 1006 + 11, device=dev).reshape(B, M, 32, d)
+    ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
+    wsm = torch.empty(tq.tq_attn_quant_workspace_bytes(sch, B, M, 32, Hkv, N), dtype=torch.uint8, device=dev)
+    om = torch.empty((B, M, 32, d), dtype=torch.bfloat16, device=dev)
+    us_m = _time_us(lambda: tq.attn_quant(qm, cache, ctx, sig, kb, vb, Hkv, out=om, workspace=wsm), 10)
+    # the pages' attention research shape: head_dim 256, GQA 6, one query, 16384 tokens
+    s256 = tq.scheme(256, 8, 3)
+    k6, v6 = synth.kv_inputs("normal", 1, 16384, 4, 256, 1007, device=dev)
+    sig256 = torch.from_numpy(synth.sign_vector(256)).to(dev)
+    c6 = tq.quantize_into_cache(k6, v6, sig256, 8, 3)
+    del k6, v6
+    q6 = synth.queries(1, 24, 256, 1008, device=dev)
+    ctx6 = torch.full((1,), 16384, dtype=torch.int32, device=dev)
+    ws6 = torch.empty(tq.tq_decode_attn_workspace_bytes(s256, 1, 24, 4, 16384), dtype=torch.uint8, device=dev)
+    o6 = torch.empty((1, 24, 256), dtype=torch.bfloat16, device=dev)
+    us_6 = _time_us(lambda: tq.decode_attn(q6, c6, ctx6, sig256, 8, 3, 4, out=o6, workspace=ws6), 20)
+    b6 = 16384 * 4 * tq.tq_row_bytes(s256)
     return {
         "append_kv": {"workload": f"decode append k{akb}v{avb} d{dd}: {L}x{T}x{H} rows, 1 token each, one launch",
                       "us": us_a, "token_heads_per_s": rows / (us_a * 1e-6),
@@ -139,6 +158,11 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
                              "us": us_r, "GBps": fb / (us_r * 1e-6) / 1e9},
         "unrotate_rows": {"workload": f"{B * Hkv * N} bf16 rows of d={d} (the rotated V window)",
                           "us": us_u, "GBps": B * Hkv * N * 4 * d / (us_u * 1e-6) / 1e9},
+        "attn_multi_query": {"workload": f"{M} causal queries per sequence over the {B}x{Hkv}x{N} k{kb}v{vb} cache, "
+                                         f"32 query heads",
+                             "us": us_m, "cache_GBps": B * Hkv * N * row_bytes / (us_m * 1e-6) / 1e9},
+        "attn_gqa6_d256": {"workload": "head_dim 256, GQA 6 (24 query / 4 kv heads), one query, 16384 tokens, k8v3",
+                           "us": us_6, "cache_GBps": b6 / (us_6 * 1e-6) / 1e9},
     }
 
 

@@ -211,6 +211,28 @@ int32_t tq_decode_attn_quant(const tq_scheme* scheme, const uint16_t* q_bf16, in
                              const int8_t* signs, uint16_t* out_bf16, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Multi-query form of tq_decode_attn_quant: n_queries >= 1 query tokens per
+ * sequence, each attending causally to the cache (the speculative / chunked
+ * decode shape; the pages' attention research runs GQA 6 at d = 256 over the
+ * quantized cache, TurboQuant page, "Packed-value decode fusion
+ * investigation").  Query m of sequence b is the cached token at position
+ * ctx_lens[b] - n_queries + m (the new tokens are already appended) and sees
+ * tokens t <= that position:
+ *   s_t = softmax_scale * q_{b,m,h} . k_hat_t      (t < ctx_lens[b] - n_queries + 1 + m)
+ *   out_{b,m,h} = signs * FWHT(sum_t softmax(s)_t z_t) / sqrt(d)
+ * A query with no visible token gets an all-zero row.
+ *   q_bf16, out_bf16 : [batch, n_queries, n_q_heads, head_dim]
+ *   workspace        : >= tq_attn_quant_workspace_bytes() bytes, 16-byte aligned
+ * Everything else as tq_decode_attn_quant, which is this call with
+ * n_queries = 1.  Returns TQ_OK or a TQ_E_* code. */
+size_t tq_attn_quant_workspace_bytes(const tq_scheme* scheme, int32_t batch, int32_t n_queries, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t max_ctx);
+int32_t tq_attn_quant(const tq_scheme* scheme, const uint16_t* q_bf16, int32_t batch, int32_t n_queries,
+                      int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache, int64_t seq_stride_rows,
+                      int64_t head_stride_rows, const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
+                      const int8_t* signs, uint16_t* out_bf16, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* Static description of a status code. */
 const char* tq_status_string(int32_t status);
 

@@ -81,6 +81,14 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.tq_decode_attn_quant.restype = ctypes.c_int32
+        L.tq_attn_quant_workspace_bytes.argtypes = [P(Scheme), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int32]
+        L.tq_attn_quant_workspace_bytes.restype = ctypes.c_size_t
+        L.tq_attn_quant.argtypes = [
+            P(Scheme), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(Planes),
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_attn_quant.restype = ctypes.c_int32
         L.tq_status_string.argtypes = [ctypes.c_int32]
         L.tq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -304,4 +312,37 @@ def unrotate_rows(x: torch.Tensor, signs: torch.Tensor, out: torch.Tensor | None
         out = torch.empty_like(x)
     r = contiguous_rows((n, 1, 1))
     _check(tq_unrotate_rows(d, x, r, signs, out, r), "tq_unrotate_rows")
+    return out
+
+
+def tq_attn_quant_workspace_bytes(scheme, batch, n_queries, n_q_heads, n_kv_heads, max_ctx) -> int:
+    return lib().tq_attn_quant_workspace_bytes(ctypes.byref(scheme), batch, n_queries, n_q_heads, n_kv_heads,
+                                               max_ctx)
+
+
+def tq_attn_quant(scheme, q, batch, n_queries, n_q_heads, n_kv_heads, cache, seq_stride_rows, head_stride_rows,
+                  ctx_lens, max_ctx, softmax_scale, signs, out, workspace, workspace_bytes, stream=None) -> int:
+    return lib().tq_attn_quant(ctypes.byref(scheme), _ptr(q), batch, n_queries, n_q_heads, n_kv_heads,
+                               ctypes.byref(cache), seq_stride_rows, head_stride_rows, _ptr(ctx_lens), max_ctx,
+                               softmax_scale, _ptr(signs), _ptr(out), _ptr(workspace), workspace_bytes,
+                               _stream(stream))
+
+
+def attn_quant(q: torch.Tensor, cache: dict, ctx_lens: torch.Tensor, signs: torch.Tensor, k_bits: int,
+               v_bits: int, n_kv_heads: int, softmax_scale: float | None = None,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Multi-query fused attention; q [B, M, Hq, d] bf16 (query m of sequence b is cached token
+    ctx_lens[b] - M + m, causal), cache planes [B, Hkv, N, bytes]; returns [B, M, Hq, d]."""
+    B, M, Hq, d = q.shape
+    N = cache["k_q"].shape[2]
+    sch = scheme(d, k_bits, v_bits)
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    if out is None:
+        out = torch.empty((B, M, Hq, d), dtype=torch.bfloat16, device=q.device)
+    ws = tq_attn_quant_workspace_bytes(sch, B, M, Hq, n_kv_heads, N)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    _check(tq_attn_quant(sch, q, B, M, Hq, n_kv_heads, planes_struct(cache), n_kv_heads * N, N, ctx_lens, N,
+                         float(softmax_scale), signs, out, workspace, workspace.numel()), "tq_attn_quant")
     return out

@@ -286,33 +286,43 @@ int32_t tq_unrotate_rows(int32_t head_dim, const uint16_t* in_bf16, const tq_row
   return hip_status(tq::launch_unrotate(a, head_dim, (hipStream_t)stream, kMaxCodecBlocks));
 }
 
-size_t tq_decode_attn_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t n_q_heads,
-                                      int32_t n_kv_heads, int32_t max_ctx) {
+size_t tq_attn_quant_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t n_queries, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t max_ctx) {
   if (check_scheme(s) != TQ_OK) return 0;
-  if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1) return 0;
+  if (batch < 0 || n_queries < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1)
+    return 0;
+  if ((int64_t)batch * n_queries * n_q_heads >= ((int64_t)1 << 31)) return 0;
   int splits = 0, tps = 0;
-  tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
-  return tq::decode_attn_part_bytes(s->head_dim, batch, n_q_heads, splits);
+  tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_queries, n_q_heads, n_kv_heads, max_ctx,
+                           &splits, &tps);
+  return tq::decode_attn_part_bytes(s->head_dim, batch, n_queries, n_q_heads, splits);
 }
 
-int32_t tq_decode_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch,
-                             int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache,
-                             int64_t seq_stride_rows, int64_t head_stride_rows,
-                             const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
-                             const int8_t* signs, uint16_t* out_bf16, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+size_t tq_decode_attn_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t max_ctx) {
+  return tq_attn_quant_workspace_bytes(s, batch, 1, n_q_heads, n_kv_heads, max_ctx);
+}
+
+int32_t tq_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, int32_t n_queries,
+                      int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache, int64_t seq_stride_rows,
+                      int64_t head_stride_rows, const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
+                      const int8_t* signs, uint16_t* out_bf16, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   int32_t st = check_scheme(s);
   if (st != TQ_OK) return st;
-  if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1 ||
+  if (batch < 0 || n_queries < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1 ||
       seq_stride_rows < 0 || head_stride_rows < 0)
     return TQ_E_SHAPE;
+  if ((int64_t)batch * n_queries * n_q_heads >= ((int64_t)1 << 31)) return TQ_E_SHAPE;
   if (batch == 0) return TQ_OK;
   if (!q_bf16 || !ctx_lens || !signs || !out_bf16) return TQ_E_NULL;
   if ((st = check_planes(cache)) != TQ_OK) return st;
   if (!aligned16(q_bf16) || !aligned16(signs) || !aligned16(out_bf16)) return TQ_E_ALIGN;
   int splits = 0, tps = 0;
-  tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_q_heads, n_kv_heads, max_ctx, &splits, &tps);
-  if (!workspace || workspace_bytes < tq::decode_attn_part_bytes(s->head_dim, batch, n_q_heads, splits))
+  tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_queries, n_q_heads, n_kv_heads, max_ctx,
+                           &splits, &tps);
+  if (!workspace ||
+      workspace_bytes < tq::decode_attn_part_bytes(s->head_dim, batch, n_queries, n_q_heads, splits))
     return TQ_E_WORKSPACE;
   if (!aligned16(workspace)) return TQ_E_ALIGN;
   tq::AttnArgs a{};
@@ -335,7 +345,18 @@ int32_t tq_decode_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t
   a.splits = splits;
   a.tokens_per_split = tps;
   a.softmax_scale = softmax_scale;
+  a.n_queries = n_queries;
   return hip_status(tq::launch_decode_attn(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream));
+}
+
+int32_t tq_decode_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache,
+                             int64_t seq_stride_rows, int64_t head_stride_rows,
+                             const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
+                             const int8_t* signs, uint16_t* out_bf16, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return tq_attn_quant(s, q_bf16, batch, 1, n_q_heads, n_kv_heads, cache, seq_stride_rows, head_stride_rows,
+                       ctx_lens, max_ctx, softmax_scale, signs, out_bf16, workspace, workspace_bytes, stream);
 }
 
 const char* tq_status_string(int32_t status) {

@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
 
   const int split = blockIdx.x % a.splits;
   int rest = blockIdx.x / a.splits;
-  const int rep = a.n_q_heads / a.n_kv_heads;
-  const int tiles = (rep + kHeadTile - 1) / kHeadTile;
+  const int rep = a.n_q_heads / a.n_kv_heads, nrow = a.n_queries * rep;
+  const int tiles = (nrow + kHeadTile - 1) / kHeadTile;
   const int tile = rest % tiles;
   rest /= tiles;
   const int g = rest % a.n_kv_heads;
@@ -85,16 +85,20 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
   int t_end = t_begin + a.tokens_per_split;
   if (t_end > ctx) t_end = ctx;
 
-  // query slice (pre-scaled into the log2 domain)
+  // query slice (pre-scaled into the log2 domain); tile row j is query
+  // jr / rep, head jr % rep of this kv head, with jr = tile * kHeadTile + j
   const float qscale = a.softmax_scale * kLog2e;
   float q[kHeadTile][8];
   bool hv[kHeadTile];
+  int lim[kHeadTile];  // tokens t < lim[j] are visible to row j
 #pragma unroll
   for (int j = 0; j < kHeadTile; ++j) {
-    const int hl = tile * kHeadTile + j;
-    hv[j] = hl < rep;
-    const int hq = g * rep + (hv[j] ? hl : 0);
-    const uint4 w = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.n_q_heads + hq) * D + 8 * sub);
+    const int jr = tile * kHeadTile + j;
+    hv[j] = jr < nrow;
+    const int mq = hv[j] ? jr / rep : 0, hq = g * rep + (hv[j] ? jr % rep : 0);
+    lim[j] = ctx - a.n_queries + 1 + mq;
+    const uint4 w = *reinterpret_cast<const uint4*>(
+        a.q + (((int64_t)b * a.n_queries + mq) * a.n_q_heads + hq) * D + 8 * sub);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) d = __builtin_fmaf(q[j][i], kh[i], d);
         d = row_sum<D>(d);
-        sc[k][j] = valid ? d : -INFINITY;
+        sc[k][j] = (valid && t < lim[j]) ? d : -INFINITY;
       }
     }
     // softmax statistics for the chunk, then the rotated-domain accumulation
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
   __syncthreads();
   for (int o = threadIdx.x; o < kHeadTile * D; o += blockDim.x) {
     const int j = o / D, e = o % D;
-    const int hl = tile * kHeadTile + j;
-    if (hl >= rep) continue;
+    const int jr = tile * kHeadTile + j;
+    if (jr >= nrow) continue;
     float mm = -INFINITY;
     for (int w = 0; w < 4; ++w)
       for (int cc = 0; cc < TPW; ++cc) mm = fmaxf(mm, red[w][cc][j][D]);
@@ -214,8 +218,8 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
           aa += red[w][cc][j][e] * f;
         }
     }
-    const int hq = g * rep + hl;
-    float* part = a.part + (((int64_t)b * a.n_q_heads + hq) * a.splits + split) * part_stride<D>();
+    const int64_t orow = ((int64_t)b * a.n_queries + jr / rep) * a.n_q_heads + g * rep + jr % rep;
+    float* part = a.part + (orow * a.splits + split) * part_stride<D>();
     part[e] = aa;
     if (e == 0) {
       part[D] = mm;
@@ -433,8 +437,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
   const int split = blockIdx.x % a.splits;
   int rest = blockIdx.x / a.splits;
-  const int rep = a.n_q_heads / a.n_kv_heads;
-  const int tiles = (rep + kHeadTile - 1) / kHeadTile;
+  const int rep = a.n_q_heads / a.n_kv_heads, nrow = a.n_queries * rep;
+  const int tiles = (nrow + kHeadTile - 1) / kHeadTile;
   const int tile = rest % tiles;
   rest /= tiles;
   const int gkv = rest % a.n_kv_heads;
@@ -474,12 +478,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
   // ---- query
   const float qscale = a.softmax_scale * kLog2e;
+  // tile row h is query jr / rep, head jr % rep of this kv head (jr = tile * 4 + h)
   auto qhead = [&](int h) -> const uint16_t* {
-    const int hl = tile * kHeadTile + h;
-    const int hq = gkv * rep + (hl < rep ? hl : 0);
-    return a.q + ((int64_t)b * a.n_q_heads + hq) * D;
+    const int jr = tile * kHeadTile + h;
+    const int mq = jr < nrow ? jr / rep : 0, hq = gkv * rep + (jr < nrow ? jr % rep : 0);
+    return a.q + (((int64_t)b * a.n_queries + mq) * a.n_q_heads + hq) * D;
   };
-  auto hvalid = [&](int h) { return tile * kHeadTile + h < rep; };
+  auto hvalid = [&](int h) { return tile * kHeadTile + h < nrow; };
   // per-head power of two (lane-group c measures head c)
   float qmax = 0.f;
   if (hvalid(c)) {
@@ -499,6 +504,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // hi in [-64, 64], lo in [-128, 127]; the key bytes are the B operand as
   // stored.  Scores come back to scale through 2^(qe - 14).
   const float smul = ldexpf(1.f, qe - 14);
+  // tokens visible to this lane-group's row (lane-group c holds row c's scores)
+  int lim_c;
+  {
+    const int jr = tile * kHeadTile + c;
+    lim_c = ctx - a.n_queries + 1 + (jr < nrow ? jr / rep : 0);
+    if (lim_c > t_end) lim_c = t_end;
+  }
   float qn[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) qn[h] = ldexpf(qscale, 14 - __builtin_amdgcn_readlane(qe, 16 * h));
@@ -683,7 +695,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       const float a13 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
       const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(a02), __float_as_uint(a13), false, false);
       const float sc = (__uint_as_float(y[0]) + __uint_as_float(y[1])) * smul;
-      Sc[tau] = (full || t < tl) ? sc : -INFINITY;
+      Sc[tau] = (cb + t < lim_c) ? sc : -INFINITY;
     }
     // ---- online softmax for head c (lane-group c)
     // The reference m_run moves only when a score exceeds it by more than
@@ -796,8 +808,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         aa += s4 * f;
       }
     }
-    const int hq = gkv * rep + tile * kHeadTile + h;
-    float* part = a.part + (((int64_t)b * a.n_q_heads + hq) * a.splits + split) * part_stride<D>();
+    const int jr = tile * kHeadTile + h;
+    const int64_t orow = ((int64_t)b * a.n_queries + jr / rep) * a.n_q_heads + gkv * rep + jr % rep;
+    float* part = a.part + (orow * a.splits + split) * part_stride<D>();
     part[e] = aa;
     if (e == 0) {
       part[D] = mm;
@@ -811,7 +824,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
   constexpr int LPR = D / 8, RPW = 64 / LPR;
   const int lane = threadIdx.x & 63, sub = lane % LPR, rw = lane / LPR;
-  const int rows = a.batch * a.n_q_heads;
+  const int rows = a.batch * a.n_queries * a.n_q_heads;
   const int r0 = ((blockIdx.x * blockDim.x + threadIdx.x) >> 6) * RPW + rw;
   const bool active = r0 < rows;
   const int r = active ? r0 : 0;
@@ -856,14 +869,14 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
 
 bool decode_attn_uses_mfma(int d, int kb, int vb) { return d <= 256 && kb == 8 && vb <= 5; }
 
-void decode_attn_geometry(int d, int kb, int vb, int batch, int n_q_heads, int n_kv_heads, int max_ctx,
-                          int* splits, int* tokens_per_split) {
+void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n_q_heads, int n_kv_heads,
+                          int max_ctx, int* splits, int* tokens_per_split) {
   // rows one block consumes per pass: four waves of 32-token steps on the
   // matrix-core path, four waves of kChunk rows per lane-group otherwise
   const bool mfma = decode_attn_uses_mfma(d, kb, vb);
   const int step = mfma ? 4 * 32 : 4 * (64 / (d / 8)) * kChunk;
   const int rep = n_q_heads / n_kv_heads;
-  const long long units = (long long)batch * n_kv_heads * ((rep + kHeadTile - 1) / kHeadTile);
+  const long long units = (long long)batch * n_kv_heads * ((n_queries * rep + kHeadTile - 1) / kHeadTile);
   // The matrix-core kernel streams through per-wave DMA stages, which pay a
   // pipeline fill per block: aim at one round of resident blocks (two per CU
   // on the 256 CUs of gfx950).  The VALU kernel prefers more, shorter blocks.
@@ -879,8 +892,8 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_q_heads, int n
   *tokens_per_split = (int)tps;
 }
 
-size_t decode_attn_part_bytes(int d, int batch, int n_q_heads, int splits) {
-  return (size_t)batch * n_q_heads * splits * (size_t)(d + 4) * sizeof(float);
+size_t decode_attn_part_bytes(int d, int batch, int n_queries, int n_q_heads, int splits) {
+  return (size_t)batch * n_queries * n_q_heads * splits * (size_t)(d + 4) * sizeof(float);
 }
 
 template <int D, int KB>
@@ -897,7 +910,7 @@ static void launch_split_kb(const AttnArgs& a, int vb, dim3 grid, hipStream_t st
 template <int D>
 static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t st) {
   const int rep = a.n_q_heads / a.n_kv_heads;
-  const int tiles = (rep + kHeadTile - 1) / kHeadTile;
+  const int tiles = (a.n_queries * rep + kHeadTile - 1) / kHeadTile;
   const dim3 grid((unsigned)(a.batch * a.n_kv_heads * tiles * a.splits));
   if constexpr (D <= 256) {
     // the DMA copies need 16-byte key rows and 4-byte aligned fp16 planes
@@ -911,7 +924,7 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
         case 4: decode_attn_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(a); break;
         default: decode_attn_mfma_kernel<D, 5><<<grid, 256, 0, st>>>(a); break;
       }
-      const int rows = a.batch * a.n_q_heads;
+      const int rows = a.batch * a.n_queries * a.n_q_heads;
       const int rows_per_block = 4 * (64 / (D / 8));
       decode_attn_combine_kernel<D><<<dim3((rows + rows_per_block - 1) / rows_per_block), 256, 0, st>>>(a);
       return hipGetLastError();
@@ -923,7 +936,7 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
     case 5: launch_split_kb<D, 5>(a, vb, grid, st); break;
     default: launch_split_kb<D, 8>(a, vb, grid, st); break;
   }
-  const int rows = a.batch * a.n_q_heads;
+  const int rows = a.batch * a.n_queries * a.n_q_heads;
   const int rows_per_block = 4 * (64 / (D / 8));
   decode_attn_combine_kernel<D><<<dim3((rows + rows_per_block - 1) / rows_per_block), 256, 0, st>>>(a);
   return hipGetLastError();

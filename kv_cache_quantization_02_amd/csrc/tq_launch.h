@@ -67,6 +67,9 @@ struct AttnArgs {
   int64_t seq_stride, head_stride;
   int32_t batch, n_q_heads, n_kv_heads, max_ctx, splits, tokens_per_split;
   float softmax_scale;
+  // Query tokens per sequence: query m of sequence b sits at position
+  // ctx_b - n_queries + m and sees the cached tokens t <= that position.
+  int32_t n_queries;
 };
 
 // Inverse rotation of bf16 rows: out = bf16(signs * FWHT(in) / sqrt(d)).
@@ -86,8 +89,8 @@ hipError_t launch_decode_attn(const AttnArgs& a, int d, int kb, int vb, hipStrea
 
 // Split-K decode geometry for a given problem (shared by the workspace query).
 bool decode_attn_uses_mfma(int d, int kb, int vb);
-void decode_attn_geometry(int d, int kb, int vb, int batch, int n_q_heads, int n_kv_heads, int max_ctx,
-                          int* splits, int* tokens_per_split);
-size_t decode_attn_part_bytes(int d, int batch, int n_q_heads, int splits);
+void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n_q_heads, int n_kv_heads,
+                          int max_ctx, int* splits, int* tokens_per_split);
+size_t decode_attn_part_bytes(int d, int batch, int n_queries, int n_q_heads, int splits);
 
 }  // namespace tq

@@ -87,3 +87,20 @@ def eager_decode_attention(q, k_hat, z_rot, signs, ctx_lens, softmax_scale):
             p, l = _softmax_weights(q[b, h], k64, float(softmax_scale))
             out[b, h] = (p @ v64) / l
     return out
+
+
+def multi_query_attention(q: np.ndarray, k_hat: np.ndarray, z_rot: np.ndarray,
+                          signs: np.ndarray, ctx_lens, softmax_scale: float) -> np.ndarray:
+    """Causal multi-query form: q [B, M, Hq, d]; query m of sequence b is the
+    cached token at ctx_b - M + m and attends to tokens t < ctx_b - M + 1 + m
+    (ctx_b clamped to the cache).  Each query is the single-query case with
+    that context, so this is the plain definition written by reuse of it;
+    a query with no visible token gives a zero row."""
+    q = np.asarray(q, np.float64)
+    B, M, Hq, d = q.shape
+    N = k_hat.shape[2]
+    out = np.zeros((B, M, Hq, d), np.float64)
+    for m in range(M):
+        lens = [min(int(ctx_lens[b]), N) - M + 1 + m for b in range(B)]
+        out[:, m] = decode_attention(q[:, m], k_hat, z_rot, signs, lens, softmax_scale)
+    return out

@@ -139,3 +139,57 @@ def test_full_size_decode_sampled():
         got = synth.bf16_bits(out[b:b + 1, g * rep:(g + 1) * rep])
         st = attention_close(got.reshape(1, rep, d), ref)
         _say(f"[gpu attn] full size (b={b}, kv head {g}): {st}")
+
+
+def run_mq_case(B, M, Hq, Hkv, N, d, kb, vb, ctx, seed, tag):
+    _say(f"[gpu attn] multi-query {tag}: B={B} M={M} Hq={Hq} Hkv={Hkv} N={N} d={d} k{kb}v{vb} ctx={ctx}")
+    k, v = synth.kv_inputs("normal", B, N, Hkv, d, seed)
+    q = synth.queries(B * M, Hq, d, seed + 7).reshape(B, M, Hq, d)
+    signs = synth.sign_vector(d)
+    sig = torch.from_numpy(signs).to(DEV)
+    cache = tq.quantize_into_cache(k.to(DEV), v.to(DEV), sig, kb, vb)
+    out = tq.attn_quant(q.to(DEV), cache, torch.tensor(ctx, dtype=torch.int32, device=DEV), sig, kb, vb, Hkv)
+    torch.cuda.synchronize()
+    kr = synth.bf16_bits(k.permute(0, 2, 1, 3).contiguous()).reshape(-1, d)
+    vr = synth.bf16_bits(v.permute(0, 2, 1, 3).contiguous()).reshape(-1, d)
+    khat, z = _oracle_cache(kr, vr, signs, kb, vb, d)
+    qf = codec.bf16_to_f32(synth.bf16_bits(q))
+    ref = attention.multi_query_attention(qf, khat.reshape(B, Hkv, N, d), z.reshape(B, Hkv, N, d),
+                                          signs, ctx, np.float32(1 / math.sqrt(d)))
+    got = synth.bf16_bits(out)
+    st = attention_close(got.reshape(B * M, Hq, d), ref.reshape(B * M, Hq, d))
+    _say(f"[gpu attn] multi-query {tag}: {st}")
+    return got, ref
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_multi_query_causal(M):
+    # the last sequence is shorter than the query chunk: its first queries see nothing
+    got, ref = run_mq_case(3, M, 8, 2, 300, 128, 8, 3, [300, 133, 2], 18, f"M{M}")
+    if M == 4:
+        assert not got[2, 0].any() and not got[2, 1].any()
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gqa6_d256(M):
+    # the pages' research attention shape: GQA 6 at head_dim 256
+    run_mq_case(2, M, 12, 2, 400, 256, 8, 3, [400, 257], 19, f"gqa6 d256 M{M}")
+
+
+def test_multi_query_valu_schemes():
+    run_mq_case(2, 3, 8, 2, 200, 128, 4, 4, [200, 77], 20, "k4v4")
+    run_mq_case(2, 3, 8, 4, 200, 512, 5, 2, [150, 200], 21, "d512 k5v2")
+
+
+def test_multi_query_matches_decode_at_m1():
+    # tq_attn_quant with one query is tq_decode_attn_quant
+    B, Hq, Hkv, N, d = 2, 8, 2, 256, 128
+    k, v = synth.kv_inputs("normal", B, N, Hkv, d, 22)
+    q = synth.queries(B, Hq, d, 29)
+    sig = torch.from_numpy(synth.sign_vector(d)).to(DEV)
+    cache = tq.quantize_into_cache(k.to(DEV), v.to(DEV), sig, 8, 3)
+    ctx = torch.tensor([256, 100], dtype=torch.int32, device=DEV)
+    a = tq.decode_attn(q.to(DEV), cache, ctx, sig, 8, 3, Hkv)
+    b = tq.attn_quant(q.to(DEV).reshape(B, 1, Hq, d), cache, ctx, sig, 8, 3, Hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.reshape(B, Hq, d).view(torch.int16))

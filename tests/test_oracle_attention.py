@@ -106,3 +106,29 @@ def test_hadamard_matrix_closed_form():
     H = attention.hadamard_matrix(8)
     assert np.array_equal(H @ H.T, 8 * np.eye(8))
     assert list(H[3]) == [1, -1, -1, 1, 1, -1, -1, 1]
+
+
+def test_multi_query_is_causal_and_reduces_to_decode():
+    # one query equals the decode form; query m of a chunk ignores the later
+    # tokens of the chunk (changing them leaves it unchanged) and equals the
+    # decode form over the prefix ending at itself
+    rng = np.random.default_rng(3)
+    B, M, Hq, Hkv, N, d = 2, 3, 4, 2, 9, 64
+    q = rng.standard_normal((B, M, Hq, d))
+    k = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    z = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    signs = np.where(rng.integers(0, 2, d) == 1, 1, -1).astype(np.int8)
+    ctx = [9, 5]
+    o = attention.multi_query_attention(q, k, z, signs, ctx, 0.125)
+    one = attention.multi_query_attention(q[:, 2:], k, z, signs, ctx, 0.125)
+    assert np.array_equal(one[:, 0], attention.decode_attention(q[:, 2], k, z, signs, ctx, 0.125))
+    assert np.array_equal(o[:, 2], one[:, 0])
+    k2, z2 = k.copy(), z.copy()
+    k2[:, :, 4:] += 10.0
+    z2[:, :, 4:] -= 7.0                     # tokens 4.. of sequence 1 are after its query 0 (position 2)
+    o2 = attention.multi_query_attention(q, k2, z2, signs, ctx, 0.125)
+    assert np.array_equal(o2[1, 0], o[1, 0])
+    assert not np.allclose(o2[1, 2], o[1, 2])
+    # a query with nothing visible is a zero row
+    o3 = attention.multi_query_attention(q, k, z, signs, [2, 9], 0.125)
+    assert not o3[0, 0].any()
