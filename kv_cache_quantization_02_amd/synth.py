@@ -124,3 +124,30 @@ WORKLOADS = {
 # Fused decode attention workload: batch, q_heads, kv_heads, head_dim, context
 DECODE_ATTN = {"batch": 16, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
                "context": 32768, "k_bits": 8, "v_bits": 3, "seed": 1006}
+
+
+# ------------------------------------------------- paper-variant parameters
+# The paper variant of the codec draws two d x d matrices once: a random
+# rotation and, for its optional residual stage, a Gaussian projection.  They
+# are random draws, so they are inputs here, given in bf16 like the cache rows.
+
+def _bf16_of_f64(a: np.ndarray) -> np.ndarray:
+    return bf16_bits(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(torch.bfloat16))
+
+
+def dense_rotation(head_dim: int, seed: int = 43) -> np.ndarray:
+    """Haar-random orthogonal [d, d] matrix as bf16 patterns: the Q factor of
+    the QR decomposition of a standard normal matrix (numpy PCG64, ``seed``),
+    its columns multiplied by the signs of R's diagonal so that the draw is
+    uniform over the orthogonal group, then rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((head_dim, head_dim))
+    q, r = np.linalg.qr(g)
+    q = q * np.where(np.diag(r) < 0, -1.0, 1.0)[None, :]
+    return _bf16_of_f64(q)
+
+
+def qjl_projection(head_dim: int, seed: int = 44) -> np.ndarray:
+    """[d, d] matrix of iid N(0, 1) entries (numpy PCG64, ``seed``) as bf16 patterns."""
+    rng = np.random.default_rng(seed)
+    return _bf16_of_f64(rng.standard_normal((head_dim, head_dim)))
