@@ -32,10 +32,18 @@ def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+# Source file of each timed kernel; its hash (with the shared headers) keys the
+# committed counter summary, so a counter run stays valid until that file changes.
+KERNEL_SOURCES = {"quantize_kernel": "tq_codec.hip", "dequantize_kernel": "tq_codec.hip",
+                  "decode_attn_mfma_kernel": "tq_attn.hip", "dense_quantize_kernel": "tq_dense.hip",
+                  "dense_dequantize_kernel": "tq_dense.hip"}
+SHARED_HEADERS = ("tq_codebooks.h", "tq_device.h", "tq_launch.h")
+
+
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_quantization_02_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in (KERNEL_SOURCES[kernel],) + SHARED_HEADERS:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
@@ -47,7 +55,9 @@ def measured_traffic(kernel: str):
     path = os.path.join(ROOT, "profiles", "traffic_counters.txt")
     if not os.path.exists(path):
         return None
-    src = source_hash()
+    if kernel not in KERNEL_SOURCES:
+        return None
+    src = source_hash(kernel)
     for line in open(path):
         if line.startswith("#") or not line.strip():
             continue
@@ -166,6 +176,42 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     }
 
 
+def measure_dense(tq, synth, k, v, dev):
+    """Timings of the paper variant (dense rotation, whole-vector norm, optional
+    QJL residual) on the prefill chunk's keys and values as one batch of rows,
+    outside the timed step: 3-bit MSE code, and 2-bit MSE + 1 QJL sign bit."""
+    import numpy as np
+    import torch
+    d = k.shape[-1]
+    x = torch.cat([k.reshape(-1, d), v.reshape(-1, d)])
+    rows = x.shape[0]
+
+    def bf(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    rot, proj = bf(synth.dense_rotation(d)), bf(synth.qjl_projection(d))
+    out = {}
+    for tag, bits, qjl, gemms_q, gemms_dq in (("mse_b3", 3, False, 1, 2), ("qjl_b2+1", 2, True, 3, 3)):
+        pj = proj if qjl else None
+        planes = tq.dense_quantize(x, rot, bits, pj)
+        back = torch.empty_like(x)
+        us_q = _time_us(lambda: tq.dense_quantize(x, rot, bits, pj, out=planes), 10)
+        us_d = _time_us(lambda: tq.dense_dequantize(planes, rot, bits, pj, out=back), 10)
+        sch = tq.dense_scheme(d, bits, qjl)
+        pb = sum(max(tq.tq_dense_plane_row_bytes(sch, i), 0) for i in range(4))
+        for name, us, gemms in (("quantize", us_q, gemms_q), ("dequantize", us_d, gemms_dq)):
+            gbps = rows * (2 * d + pb) / (us * 1e-6) / 1e9
+            tflops = rows * gemms * 2 * d * d / (us * 1e-6) / 1e12
+            out[f"dense_{name}_{tag}"] = {
+                "workload": f"{rows} rows (prefill keys + values), d={d}, {tag}",
+                "kernel": f"dense_{name}_kernel<{d},{bits},{int(qjl)}>", "us": us,
+                "rows_per_s": rows / (us * 1e-6), "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBS,
+                "mfma_bf16_TFLOPs_executed": tflops, "frac_of_bf16_mfma_peak": tflops / 2500.0,
+                "plane_bytes_per_row": pb}
+        del planes, back
+    del x
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +319,7 @@ def main():
     next_rows = None
     if not args.no_next:
         next_rows = measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev)
+        next_rows.update(measure_dense(tq, synth, k, v, dev))
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)

@@ -44,8 +44,8 @@ extern "C" {
 #endif
 
 #define TQ_OK 0
-#define TQ_E_HEAD_DIM (-1)  /* head_dim not in {64, 128, 256, 512}              */
-#define TQ_E_BITS (-2)      /* k_bits not in {2,4,5,8} or v_bits not in {2,3,4,5,8} */
+#define TQ_E_HEAD_DIM (-1)  /* head_dim not served by the call (see each call)   */
+#define TQ_E_BITS (-2)      /* bit widths not served by the call (see each call) */
 #define TQ_E_NULL (-3)      /* a required pointer is NULL                        */
 #define TQ_E_SHAPE (-4)     /* negative count/stride, mismatched counts, Hq % Hkv */
 #define TQ_E_ALIGN (-5)     /* a base pointer breaks the alignment rules below   */
@@ -232,6 +232,67 @@ int32_t tq_attn_quant(const tq_scheme* scheme, const uint16_t* q_bf16, int32_t b
                       int64_t head_stride_rows, const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
                       const int8_t* signs, uint16_t* out_bf16, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Paper variant (TurboQuant KV design pages, "Oracle chain": the paper's own
+ * codec -- a dense random rotation from the QR decomposition of a Gaussian
+ * matrix, no groups, the same codec for keys and values, an optional QJL
+ * residual stage; the third design listed there supplies the whole-vector
+ * norm and the MSE / Prod split).  Per row x of head_dim d:
+ *   norm = ||x||_2;  y = P x;  idx_i = #{boundaries < sqrt(d) * y_i / norm}
+ *   (the N(0,1) Lloyd-Max table of `bits`, tq_codebook; a zero row codes
+ *   u = 0).  With qjl = 1:  rho = y - norm * c[idx] / sqrt(d);
+ *   gamma = ||rho||_2;  q_i = [(S rho)_i >= 0].
+ * Dequantization: y_hat = norm * c[idx] / sqrt(d)
+ *   (+ sqrt(pi/2) / d * gamma * S^T (2q - 1) with qjl);  x_hat = P^T y_hat.
+ * P (the rotation) and S (the Gaussian projection) are caller-drawn d x d
+ * bf16 matrices, row-major, 16-byte aligned device arrays.  Products are
+ * float32 sums of exact bf16 products; float32 operands (residual,
+ * reconstruction) enter as bf16 hi + lo pairs.  Served: d in {64, 128, 256},
+ * bits in {1, 2, 3, 4}, qjl only for d <= 128 (the matrices stay resident in
+ * one compute unit's LDS).  Inputs are finite, with ||x||^2 inside float32.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t head_dim;
+  int32_t bits;  /* MSE index width */
+  int32_t qjl;   /* 0 or 1: add the QJL residual stage */
+} tq_dense_scheme;
+
+/* Planes of the paper variant, addressed by one row index.  Per row:
+ *   idx   : uint8[d*bits/8], the packed little-endian bitstream of tq_planes
+ *   norm  : float32
+ *   qjl   : uint8[d/8], bit i of the stream = q_i (qjl schemes only)
+ *   gamma : float32 (qjl schemes only)
+ * idx and qjl are 8-byte aligned, norm and gamma 4-byte aligned. */
+typedef struct {
+  void* idx;
+  float* norm;
+  void* qjl;
+  float* gamma;
+} tq_dense_planes;
+
+enum { TQ_DENSE_IDX = 0, TQ_DENSE_NORM, TQ_DENSE_QJL, TQ_DENSE_GAMMA };
+
+/* TQ_OK, TQ_E_NULL, TQ_E_HEAD_DIM (d not in {64,128,256}, or qjl with
+ * d > 128) or TQ_E_BITS (bits not in 1..4, qjl not 0/1).  Host only. */
+int32_t tq_dense_check_scheme(const tq_dense_scheme* scheme);
+
+/* Bytes per row of plane TQ_DENSE_* (0 for the QJL planes of a scheme
+ * without them), or a negative TQ_E_* code.  Host only. */
+int64_t tq_dense_plane_row_bytes(const tq_dense_scheme* scheme, int32_t plane);
+
+/* Quantize bf16 rows (addressed by *in_rows) into the planes (addressed by
+ * *out_rows, same counts).  proj may be NULL unless scheme->qjl.
+ * Returns TQ_OK or a TQ_E_* code. */
+int32_t tq_dense_quantize(const tq_dense_scheme* scheme, const uint16_t* x_bf16, const tq_rows* in_rows,
+                          const uint16_t* rot_bf16, const uint16_t* proj_bf16, const tq_dense_planes* out,
+                          const tq_rows* out_rows, void* stream);
+
+/* Rebuild bf16 rows x_hat (round to nearest even, NaN as 0x7FC0) from the
+ * planes.  Returns TQ_OK or a TQ_E_* code. */
+int32_t tq_dense_dequantize(const tq_dense_scheme* scheme, const tq_dense_planes* in, const tq_rows* in_rows,
+                            const uint16_t* rot_bf16, const uint16_t* proj_bf16, uint16_t* x_bf16,
+                            const tq_rows* out_rows, void* stream);
 
 /* Static description of a status code. */
 const char* tq_status_string(int32_t status);

@@ -36,6 +36,17 @@ class Rows(ctypes.Structure):
                 ("n_seq", "n_tok", "n_head", "seq_stride", "tok_stride", "head_stride")]
 
 
+class DenseScheme(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32), ("qjl", ctypes.c_int32)]
+
+
+DENSE_PLANES = ("idx", "norm", "qjl", "gamma")
+
+
+class DensePlanes(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in DENSE_PLANES]
+
+
 _lib = None
 
 
@@ -89,6 +100,16 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.tq_attn_quant.restype = ctypes.c_int32
+        L.tq_dense_check_scheme.argtypes = [P(DenseScheme)]
+        L.tq_dense_check_scheme.restype = ctypes.c_int32
+        L.tq_dense_plane_row_bytes.argtypes = [P(DenseScheme), ctypes.c_int32]
+        L.tq_dense_plane_row_bytes.restype = ctypes.c_int64
+        L.tq_dense_quantize.argtypes = [P(DenseScheme), ctypes.c_void_p, P(Rows), ctypes.c_void_p, ctypes.c_void_p,
+                                        P(DensePlanes), P(Rows), ctypes.c_void_p]
+        L.tq_dense_quantize.restype = ctypes.c_int32
+        L.tq_dense_dequantize.argtypes = [P(DenseScheme), P(DensePlanes), P(Rows), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, P(Rows), ctypes.c_void_p]
+        L.tq_dense_dequantize.restype = ctypes.c_int32
         L.tq_status_string.argtypes = [ctypes.c_int32]
         L.tq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -345,4 +366,83 @@ def attn_quant(q: torch.Tensor, cache: dict, ctx_lens: torch.Tensor, signs: torc
         workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
     _check(tq_attn_quant(sch, q, B, M, Hq, n_kv_heads, planes_struct(cache), n_kv_heads * N, N, ctx_lens, N,
                          float(softmax_scale), signs, out, workspace, workspace.numel()), "tq_attn_quant")
+    return out
+
+
+# -------------------------------------------------------------- paper variant
+def tq_dense_check_scheme(scheme: DenseScheme) -> int:
+    return lib().tq_dense_check_scheme(ctypes.byref(scheme))
+
+
+def tq_dense_plane_row_bytes(scheme: DenseScheme, plane: int) -> int:
+    return lib().tq_dense_plane_row_bytes(ctypes.byref(scheme), plane)
+
+
+def tq_dense_quantize(scheme, x, in_rows, rot, proj, out, out_rows, stream=None) -> int:
+    return lib().tq_dense_quantize(ctypes.byref(scheme), _ptr(x), ctypes.byref(in_rows), _ptr(rot), _ptr(proj),
+                                   ctypes.byref(out), ctypes.byref(out_rows), _stream(stream))
+
+
+def tq_dense_dequantize(scheme, planes, in_rows, rot, proj, x, out_rows, stream=None) -> int:
+    return lib().tq_dense_dequantize(ctypes.byref(scheme), ctypes.byref(planes), ctypes.byref(in_rows), _ptr(rot),
+                                     _ptr(proj), _ptr(x), ctypes.byref(out_rows), _stream(stream))
+
+
+def dense_scheme(head_dim: int, bits: int, qjl: bool = False) -> DenseScheme:
+    return DenseScheme(head_dim, bits, 1 if qjl else 0)
+
+
+def alloc_dense_planes(sch: DenseScheme, lead_shape, device) -> dict:
+    """Empty paper-variant planes of shape lead_shape + [row bytes] (norm, gamma as float32 [...])."""
+    out = {}
+    for i, name in enumerate(DENSE_PLANES):
+        nbytes = tq_dense_plane_row_bytes(sch, i)
+        if nbytes < 0:
+            raise TQError(nbytes, "tq_dense_plane_row_bytes")
+        if nbytes == 0:
+            continue
+        if name in ("idx", "qjl"):
+            out[name] = torch.empty(tuple(lead_shape) + (nbytes,), dtype=torch.uint8, device=device)
+        else:
+            out[name] = torch.empty(tuple(lead_shape), dtype=torch.float32, device=device)
+    return out
+
+
+def dense_planes_struct(planes: dict) -> DensePlanes:
+    return DensePlanes(*[_ptr(planes.get(n)) for n in DENSE_PLANES])
+
+
+def _lead_rows(lead) -> Rows:
+    lead = tuple(lead)
+    while len(lead) < 3:
+        lead = (1,) + lead
+    if len(lead) != 3:
+        raise ValueError("rows must be given as at most three leading dims")
+    return contiguous_rows(lead)
+
+
+def dense_quantize(x: torch.Tensor, rot: torch.Tensor, bits: int, proj: torch.Tensor | None = None,
+                   out: dict | None = None) -> dict:
+    """Paper-variant codec of contiguous bf16 rows [..., d] (at most three leading dims):
+    rot (and proj for the QJL stage) are bf16 [d, d]."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    sch = dense_scheme(x.shape[-1], bits, proj is not None)
+    lead = x.shape[:-1]
+    if out is None:
+        out = alloc_dense_planes(sch, lead, x.device)
+    r = _lead_rows(lead)
+    _check(tq_dense_quantize(sch, x, r, rot, proj, dense_planes_struct(out), r), "tq_dense_quantize")
+    return out
+
+
+def dense_dequantize(planes: dict, rot: torch.Tensor, bits: int, proj: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 rows [..., d] rebuilt from contiguous paper-variant planes."""
+    d = rot.shape[-1]
+    sch = dense_scheme(d, bits, proj is not None)
+    lead = planes["norm"].shape
+    if out is None:
+        out = torch.empty(tuple(lead) + (d,), dtype=torch.bfloat16, device=planes["norm"].device)
+    r = _lead_rows(lead)
+    _check(tq_dense_dequantize(sch, dense_planes_struct(planes), r, rot, proj, out, r), "tq_dense_dequantize")
     return out

@@ -359,11 +359,90 @@ int32_t tq_decode_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t
                        ctx_lens, max_ctx, softmax_scale, signs, out_bf16, workspace, workspace_bytes, stream);
 }
 
+int32_t tq_dense_check_scheme(const tq_dense_scheme* s) {
+  if (!s) return TQ_E_NULL;
+  const int d = s->head_dim;
+  if (d != 64 && d != 128 && d != 256) return TQ_E_HEAD_DIM;
+  if (s->bits < 1 || s->bits > 4 || (s->qjl != 0 && s->qjl != 1)) return TQ_E_BITS;
+  if (s->qjl && d > 128) return TQ_E_HEAD_DIM;
+  return TQ_OK;
+}
+
+int64_t tq_dense_plane_row_bytes(const tq_dense_scheme* s, int32_t plane) {
+  const int32_t st = tq_dense_check_scheme(s);
+  if (st != TQ_OK) return st;
+  switch (plane) {
+    case TQ_DENSE_IDX: return (int64_t)s->head_dim * s->bits / 8;
+    case TQ_DENSE_NORM: return 4;
+    case TQ_DENSE_QJL: return s->qjl ? s->head_dim / 8 : 0;
+    case TQ_DENSE_GAMMA: return s->qjl ? 4 : 0;
+    default: return TQ_E_PLANE;
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t check_dense_call(const tq_dense_scheme* s, const uint16_t* x, const uint16_t* rot, const uint16_t* proj,
+                         const tq_dense_planes* p, const tq_rows* x_rows, const tq_rows* p_rows,
+                         tq::DenseArgs* a) {
+  int32_t st = tq_dense_check_scheme(s);
+  if (st != TQ_OK) return st;
+  if (!x || !rot || !p || (s->qjl && !proj)) return TQ_E_NULL;
+  if (!p->idx || !p->norm || (s->qjl && (!p->qjl || !p->gamma))) return TQ_E_NULL;
+  if (!aligned16(x) || !aligned16(rot) || (s->qjl && !aligned16(proj))) return TQ_E_ALIGN;
+  if (!aligned(p->idx, 8) || !aligned(p->norm, 4) || (s->qjl && (!aligned(p->qjl, 8) || !aligned(p->gamma, 4))))
+    return TQ_E_ALIGN;
+  uint32_t rows = 0, rows_p = 0;
+  tq::RowSplit split{};
+  if ((st = check_rows(x_rows, &rows, &split)) != TQ_OK) return st;
+  if ((st = check_rows(p_rows, &rows_p, &split)) != TQ_OK) return st;
+  if (!same_counts(x_rows, p_rows)) return TQ_E_SHAPE;
+  a->rot = rot;
+  a->proj = s->qjl ? proj : nullptr;
+  a->idx = (uint8_t*)p->idx;
+  a->norm = p->norm;
+  a->qjl = s->qjl ? (uint8_t*)p->qjl : nullptr;
+  a->gamma = s->qjl ? p->gamma : nullptr;
+  a->rows = rows;
+  a->split = split;
+  a->x_map = map_of(x_rows);
+  a->plane_map = map_of(p_rows);
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tq_dense_quantize(const tq_dense_scheme* s, const uint16_t* x_bf16, const tq_rows* in_rows,
+                          const uint16_t* rot_bf16, const uint16_t* proj_bf16, const tq_dense_planes* out,
+                          const tq_rows* out_rows, void* stream) {
+  tq::DenseArgs a{};
+  const int32_t st = check_dense_call(s, x_bf16, rot_bf16, proj_bf16, out, in_rows, out_rows, &a);
+  if (st != TQ_OK) return st;
+  if (a.rows == 0) return TQ_OK;
+  a.x = x_bf16;
+  return hip_status(tq::launch_dense_quantize(a, s->head_dim, s->bits, s->qjl != 0, (hipStream_t)stream));
+}
+
+int32_t tq_dense_dequantize(const tq_dense_scheme* s, const tq_dense_planes* in, const tq_rows* in_rows,
+                            const uint16_t* rot_bf16, const uint16_t* proj_bf16, uint16_t* x_bf16,
+                            const tq_rows* out_rows, void* stream) {
+  tq::DenseArgs a{};
+  const int32_t st = check_dense_call(s, x_bf16, rot_bf16, proj_bf16, in, out_rows, in_rows, &a);
+  if (st != TQ_OK) return st;
+  if (a.rows == 0) return TQ_OK;
+  a.x_out = x_bf16;
+  return hip_status(tq::launch_dense_dequantize(a, s->head_dim, s->bits, s->qjl != 0, (hipStream_t)stream));
+}
+
 const char* tq_status_string(int32_t status) {
   switch (status) {
     case TQ_OK: return "ok";
-    case TQ_E_HEAD_DIM: return "head_dim must be 64, 128, 256 or 512";
-    case TQ_E_BITS: return "k_bits must be 2, 4, 5 or 8 and v_bits 2, 3, 4, 5 or 8";
+    case TQ_E_HEAD_DIM: return "head_dim not served by this call (64, 128, 256 or 512; paper variant 64..256, QJL <= 128)";
+    case TQ_E_BITS: return "k_bits must be 2, 4, 5 or 8 and v_bits 2, 3, 4, 5 or 8 (paper variant: bits 1..4, qjl 0 or 1)";
     case TQ_E_NULL: return "a required pointer is null";
     case TQ_E_SHAPE: return "invalid counts or strides";
     case TQ_E_ALIGN: return "a base pointer is not suitably aligned";

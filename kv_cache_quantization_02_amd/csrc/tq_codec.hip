@@ -153,19 +153,6 @@ __device__ __forceinline__ float fwht_group(float (&w)[32], int lane) {
   return sigma;
 }
 
-// ------------------------------------------------------------ row helpers
-__device__ __forceinline__ void split_row(uint32_t r, const RowSplit& rs, uint32_t& s, uint32_t& t,
-                                          uint32_t& h) {
-  const uint32_t st = fast_div(r, rs.div_head);
-  h = r - st * rs.div_head.d;
-  s = fast_div(st, rs.div_tok);
-  t = st - s * rs.div_tok.d;
-}
-
-__device__ __forceinline__ int64_t row_index(const RowMap& m, uint32_t s, uint32_t t, uint32_t h) {
-  return (int64_t)s * m.seq_stride + (int64_t)t * m.tok_stride + (int64_t)h * m.head_stride;
-}
-
 // 32 bf16 (64 bytes) -> 16 raw words.
 __device__ __forceinline__ void load_group(const uint16_t* p, uint32_t (&u)[16]) {
   const uint4* q = reinterpret_cast<const uint4*>(p);

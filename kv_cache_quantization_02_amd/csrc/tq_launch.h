@@ -15,6 +15,19 @@ struct RowSplit {
   FastDiv div_tok;   // divides by n_tok
 };
 
+// Row r -> (s, t, h), and the buffer row index of (s, t, h) under a map.
+__device__ __forceinline__ void split_row(uint32_t r, const RowSplit& rs, uint32_t& s, uint32_t& t,
+                                          uint32_t& h) {
+  const uint32_t st = fast_div(r, rs.div_head);
+  h = r - st * rs.div_head.d;
+  s = fast_div(st, rs.div_tok);
+  t = st - s * rs.div_tok.d;
+}
+
+__device__ __forceinline__ int64_t row_index(const RowMap& m, uint32_t s, uint32_t t, uint32_t h) {
+  return (int64_t)s * m.seq_stride + (int64_t)t * m.tok_stride + (int64_t)h * m.head_stride;
+}
+
 struct QuantArgs {
   const uint16_t* k;
   const uint16_t* v;
@@ -82,10 +95,30 @@ struct UnrotateArgs {
   RowMap in_map, out_map;
 };
 
+// Paper variant (dense rotation, one norm per row, optional QJL residual).
+// Quantize reads bf16 rows x through x_map and writes the planes through
+// plane_map; dequantize reads the planes and writes bf16 rows to x_out.
+struct DenseArgs {
+  const uint16_t* x;
+  uint16_t* x_out;
+  const uint16_t* rot;   // [d][d] bf16, row-major
+  const uint16_t* proj;  // [d][d] bf16, row-major (QJL only)
+  uint8_t* idx;          // d*bits/8 bytes per row
+  float* norm;
+  uint8_t* qjl;          // d/8 bytes per row (QJL only)
+  float* gamma;          // (QJL only)
+  uint32_t rows;
+  RowSplit split;
+  RowMap x_map, plane_map;
+};
+
 hipError_t launch_quantize(const QuantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
 hipError_t launch_unrotate(const UnrotateArgs& a, int d, hipStream_t st, int max_blocks);
 hipError_t launch_dequantize(const DequantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
 hipError_t launch_decode_attn(const AttnArgs& a, int d, int kb, int vb, hipStream_t st);
+
+hipError_t launch_dense_quantize(const DenseArgs& a, int d, int bits, bool qjl, hipStream_t st);
+hipError_t launch_dense_dequantize(const DenseArgs& a, int d, int bits, bool qjl, hipStream_t st);
 
 // Split-K decode geometry for a given problem (shared by the workspace query).
 bool decode_attn_uses_mfma(int d, int kb, int vb);

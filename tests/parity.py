@@ -92,3 +92,100 @@ def attention_close(gpu_bits: np.ndarray, ref64: np.ndarray) -> dict:
     num = np.linalg.norm(g - ref64, axis=-1)
     den = np.maximum(np.linalg.norm(ref64, axis=-1), 1e-30)
     return {"max_rel_l2": float(np.max(num / den)), "max_abs_err": float(np.max(err))}
+
+
+# ------------------------------------------------------------ paper variant
+# The paper variant's products are float32 sums of exact bf16 products, so the
+# GPU and the float64 oracle may take a different side of a decision point
+# only within the sum's rounding bound.  Per element the bound is built from
+# the oracle's own float64 terms: gamma_n * sum |terms| for an n-term float32
+# sum (gamma_n = n * 2^-23, the rounding of an MFMA accumulation step taken as
+# a full ulp), plus 2^-17 of every operand split into bf16 hi + lo.
+U = 2.0 ** -24
+
+
+def _gamma(n):
+    return n * 2.0 ** -23
+
+
+def compare_dense_planes(gpu: dict, ref: dict, x_bits, rot_bits, proj_bits, d: int, bits: int) -> dict:
+    """gpu: numpy planes {idx [R, d*bits/8] u8, norm [R] f32, qjl, gamma}; ref: dense.quantize output."""
+    from oracle import dense
+    x = codec.bf16_to_f32(x_bits).astype(np.float64)
+    P = codec.bf16_to_f32(rot_bits).astype(np.float64)
+    n_ref = np.sqrt(np.sum(x * x, axis=1))
+    n_gpu = np.asarray(gpu["norm"], np.float64).reshape(-1)
+    tol_n = (d + 8) * U * n_ref
+    assert np.all(np.abs(n_gpu - n_ref) <= tol_n), f"norm: max err {np.max(np.abs(n_gpu - n_ref) - tol_n)} over bound"
+    # index decisions: u = sqrt(d) y / norm against the boundaries
+    ey = _gamma(d) * (np.abs(x) @ np.abs(P).T)                       # |y_gpu - y| bound
+    safe = np.where(n_ref > 0, n_ref, 1.0)[:, None]
+    eps_u = np.sqrt(d) * ey / safe + np.abs(ref["u"]) * (d + 16) * U
+    gi = codec.unpack_bits(np.asarray(gpu["idx"]).reshape(len(x), -1), bits, d).astype(np.int64)
+    ri = ref["idx"]
+    diff = gi != ri
+    out = {"index_ties": int(diff.sum())}
+    if diff.any():
+        _, bnd = codebook(bits)
+        k = np.minimum(gi[diff], ri[diff])
+        one = np.abs(gi[diff] - ri[diff]) == 1
+        near = np.abs(ref["u"][diff] - bnd.astype(np.float64)[np.clip(k, 0, len(bnd) - 1)]) <= eps_u[diff]
+        assert np.all(one & near), (f"index mismatches outside the rounding band: {np.sum(~(one & near))} of "
+                                    f"{diff.sum()}; u={ref['u'][diff][~(one & near)][:5]}")
+    if "qjl" not in ref:
+        if not diff.any():
+            assert np.array_equal(np.asarray(gpu["idx"]).reshape(len(x), -1), ref["idx_packed"])
+        return out
+    S = codec.bf16_to_f32(proj_bits).astype(np.float64)
+    rows_ok = ~diff.any(axis=1)
+    # residual: y error, the norm's error through y_hat, one rounding of the fma
+    cent, _ = codebook(bits)
+    c = cent.astype(np.float64)[ri]
+    drho = ey + np.abs(c) / np.sqrt(d) * (tol_n[:, None] + (d + 16) * U * n_ref[:, None]) + U * np.abs(ref["rho"])
+    eps_s = (np.abs(drho) @ np.abs(S).T + (2.0 ** -17 + _gamma(2 * d)) * (np.abs(ref["rho"]) @ np.abs(S).T))
+    gq = codec.unpack_bits(np.asarray(gpu["qjl"]).reshape(len(x), -1), 1, d).astype(np.int64)
+    qd = (gq != ref["qjl"]) & rows_ok[:, None]
+    if qd.any():
+        near = np.abs(ref["s"][qd]) <= eps_s[qd]
+        assert np.all(near), (f"QJL sign mismatches outside the rounding band: {np.sum(~near)} of {qd.sum()}; "
+                              f"s={ref['s'][qd][~near][:5]} eps={eps_s[qd][~near][:5]}")
+    out["sign_ties"] = int(qd.sum())
+    out["rows_with_index_ties"] = int((~rows_ok).sum())
+    g_gpu = np.asarray(gpu["gamma"], np.float64).reshape(-1)
+    g_ref = np.sqrt(np.sum(ref["rho"] ** 2, axis=1))
+    tol_g = np.sqrt(np.sum(drho ** 2, axis=1)) + (d + 8) * U * g_ref
+    okg = np.abs(g_gpu - g_ref) <= tol_g
+    assert np.all(okg[rows_ok]), f"gamma outside bound: {np.sum(~okg[rows_ok])} rows"
+    # a tie moves the residual by at most one centroid gap: gamma stays finite and close
+    if (~rows_ok).any():
+        gap = np.max(np.diff(cent.astype(np.float64))) * n_ref[~rows_ok] / np.sqrt(d)
+        assert np.all(np.abs(g_gpu[~rows_ok] - g_ref[~rows_ok]) <= gap * np.sqrt(d) + tol_g[~rows_ok])
+    return out
+
+
+def compare_dense_dequant(gpu_bits, planes: dict, rot_bits, proj_bits, d: int, bits: int) -> dict:
+    """GPU bf16 reconstruction of the oracle's planes against the float64 oracle, element-wise:
+    |gpu - ref| <= eps + ulp_bf16(|ref| + eps) / 2, eps the float32 bound of the two products."""
+    from oracle import dense
+    qjl = planes.get("qjl")
+    gamma = planes.get("gamma")
+    y_hat = dense.rotated_reconstruction(planes["idx"], planes["norm"], bits, d, qjl, gamma, proj_bits)
+    P = codec.bf16_to_f32(rot_bits).astype(np.float64)
+    ref = y_hat @ P
+    # float32 errors of the rotated-domain vector the kernel builds: the scale
+    # norm / sqrt(d) and its product (4 ulp), and with QJL the float32 sum
+    # S^T q (exact +-S terms) scaled by sqrt(pi/2)/d * gamma (3 ulp)
+    mse = dense.rotated_reconstruction(planes["idx"], planes["norm"], bits, d)
+    dy = 4 * U * (np.abs(mse) + np.abs(y_hat))
+    if qjl is not None:
+        S = codec.bf16_to_f32(proj_bits).astype(np.float64)
+        coef = np.sqrt(np.pi / 2) / d * np.asarray(gamma, np.float64)[:, None]
+        dy = dy + coef * (_gamma(d) + 3 * U) * np.sum(np.abs(S), axis=0)[None, :]
+    eps = (dy + (2.0 ** -17 + _gamma(2 * d) + 2 * U) * np.abs(y_hat)) @ np.abs(P)
+    g = codec.bf16_to_f32(_u16(gpu_bits).reshape(ref.shape)).astype(np.float64)
+    tol = eps + 0.5 * bf16_ulp(np.abs(ref) + eps)
+    bad = np.abs(g - ref) > tol
+    assert not bad.any(), (f"dequant outside bound: {bad.sum()} elements; gpu={g[bad][:5]} ref={ref[bad][:5]} "
+                           f"tol={tol[bad][:5]}")
+    exact = codec.f32_to_bf16(ref.astype(np.float32)) == _u16(gpu_bits).reshape(ref.shape)
+    return {"not_bit_exact": int((~exact).sum()), "max_err_over_tol": float(np.max(np.abs(g - ref) / tol))}

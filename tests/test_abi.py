@@ -172,3 +172,45 @@ def test_unrotate_validation_errors_without_gpu():
     assert tq.tq_unrotate_rows(128, FAKE, r, FAKE, FAKE, tq.Rows(1, 4, 3, 12, 3, 1)) == -4
     z = tq.Rows(0, 4, 2, 8, 2, 1)
     assert tq.tq_unrotate_rows(128, FAKE, z, FAKE, FAKE, z) == 0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("qjl", [0, 1])
+def test_dense_row_bytes_match_oracle(d, bits, qjl):
+    from oracle import dense
+    s = tq.dense_scheme(d, bits, bool(qjl))
+    if qjl and d > 128:
+        assert tq.tq_dense_check_scheme(s) == -1
+        return
+    assert tq.tq_dense_check_scheme(s) == 0
+    want = dense.plane_row_bytes(d, bits, bool(qjl))
+    got = {n: tq.tq_dense_plane_row_bytes(s, i) for i, n in enumerate(tq.DENSE_PLANES)}
+    assert got == {n: want.get(n, 0) for n in tq.DENSE_PLANES}
+    assert tq.tq_dense_plane_row_bytes(s, 4) == -8
+
+
+@pytest.mark.parametrize("bad,code", [((512, 3, 0), -1), ((96, 3, 0), -1), ((256, 3, 1), -1), ((128, 0, 0), -2),
+                                      ((128, 5, 0), -2), ((128, 3, 2), -2)])
+def test_dense_scheme_validation(bad, code):
+    assert tq.tq_dense_check_scheme(tq.DenseScheme(*bad)) == code
+
+
+def test_dense_validation_errors_without_gpu():
+    s = tq.dense_scheme(128, 3, True)
+    r = tq.Rows(1, 4, 2, 8, 2, 1)
+    good = tq.DensePlanes(FAKE, FAKE, FAKE, FAKE)
+    assert tq.tq_dense_quantize(tq.dense_scheme(512, 3), FAKE, r, FAKE, None, good, r) == -1
+    assert tq.tq_dense_quantize(s, FAKE, r, FAKE, None, good, r) == -3           # QJL needs the projection
+    assert tq.tq_dense_quantize(s, None, r, FAKE, FAKE, good, r) == -3
+    assert tq.tq_dense_quantize(s, FAKE, r, FAKE, FAKE, tq.DensePlanes(FAKE, FAKE, None, FAKE), r) == -3
+    assert tq.tq_dense_quantize(s, FAKE + 8, r, FAKE, FAKE, good, r) == -5
+    assert tq.tq_dense_quantize(s, FAKE, r, FAKE + 2, FAKE, good, r) == -5
+    assert tq.tq_dense_quantize(s, FAKE, r, FAKE, FAKE, tq.DensePlanes(FAKE + 4, FAKE, FAKE, FAKE), r) == -5
+    assert tq.tq_dense_quantize(s, FAKE, r, FAKE, FAKE, tq.DensePlanes(FAKE, FAKE + 2, FAKE, FAKE), r) == -5
+    assert tq.tq_dense_quantize(s, FAKE, r, FAKE, FAKE, good, tq.Rows(1, 4, 3, 12, 3, 1)) == -4
+    assert tq.tq_dense_dequantize(s, good, r, FAKE, None, FAKE, r) == -3
+    assert tq.tq_dense_dequantize(s, good, r, FAKE, FAKE, FAKE + 8, r) == -5
+    z = tq.Rows(0, 4, 2, 8, 2, 1)
+    assert tq.tq_dense_quantize(s, FAKE, z, FAKE, FAKE, good, z) == 0
+    assert tq.tq_dense_dequantize(s, good, z, FAKE, FAKE, FAKE, z) == 0
