@@ -435,12 +435,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   float(*const stats)[4][2] = reinterpret_cast<float(*)[4][2]>(lds_all + C::OFF_STATS);
   uint8_t* const smem = lds_all + C::OFF_BUF;
 
-  const int split = blockIdx.x % a.splits;
-  int rest = blockIdx.x / a.splits;
   const int rep = a.n_q_heads / a.n_kv_heads, nrow = a.n_queries * rep;
   const int tiles = (nrow + kHeadTile - 1) / kHeadTile;
-  const int tile = rest % tiles;
-  rest /= tiles;
+  // The tiles of one (sequence, kv head, split) stream the same cache rows.
+  // Blocks are dealt to the 8 XCDs round robin (block i to XCD i mod 8), so
+  // when the grid allows, the tiles of a group take blocks 8 apart: they run
+  // on one XCD, together, and the later tiles find the rows in its L2.
+  int group, tile;
+  if (tiles > 1 && gridDim.x % (8u * tiles) == 0) {
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    tile = j % tiles;
+    group = (j / tiles) * 8 + xcd;
+  } else {
+    tile = (blockIdx.x / a.splits) % tiles;
+    group = (blockIdx.x / a.splits / tiles) * a.splits + blockIdx.x % a.splits;
+  }
+  const int split = group % a.splits;
+  int rest = group / a.splits;
   const int gkv = rest % a.n_kv_heads;
   const int b = rest / a.n_kv_heads;
   const int lane = threadIdx.x & 63;
@@ -829,20 +840,46 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
   const bool active = r0 < rows;
   const int r = active ? r0 : 0;
   const float* part = a.part + (int64_t)r * a.splits * part_stride<D>();
+  // splits are read SB at a time so that their loads are in flight together;
+  // the merge itself runs in split order
+  constexpr int SB = 8;
   float mm = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mm = fmaxf(mm, part[s * part_stride<D>() + D]);
+  for (int s0 = 0; s0 < a.splits; s0 += SB) {
+    float mv[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) mv[j] = (s0 + j < a.splits) ? part[(s0 + j) * part_stride<D>() + D] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) mm = fmaxf(mm, mv[j]);
+  }
   float ll = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (mm != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float* ps = part + s * part_stride<D>();
-      const float f = exp2f(ps[D] - mm);
-      ll += ps[D + 1] * f;
-      const float4 x0 = *reinterpret_cast<const float4*>(ps + 8 * sub);
-      const float4 x1 = *reinterpret_cast<const float4*>(ps + 8 * sub + 4);
-      acc[0] += x0.x * f; acc[1] += x0.y * f; acc[2] += x0.z * f; acc[3] += x0.w * f;
-      acc[4] += x1.x * f; acc[5] += x1.y * f; acc[6] += x1.z * f; acc[7] += x1.w * f;
+    for (int s0 = 0; s0 < a.splits; s0 += SB) {
+      float ms[SB], ls[SB];
+      float4 x0[SB], x1[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        if (s0 + j < a.splits) {
+          const float* ps = part + (s0 + j) * part_stride<D>();
+          ms[j] = ps[D];
+          ls[j] = ps[D + 1];
+          x0[j] = *reinterpret_cast<const float4*>(ps + 8 * sub);
+          x1[j] = *reinterpret_cast<const float4*>(ps + 8 * sub + 4);
+        } else {
+          ms[j] = -INFINITY;
+          ls[j] = 0.f;
+          x0[j] = x1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        if (s0 + j >= a.splits) break;
+        const float f = exp2f(ms[j] - mm);
+        ll += ls[j] * f;
+        acc[0] += x0[j].x * f; acc[1] += x0[j].y * f; acc[2] += x0[j].z * f; acc[3] += x0[j].w * f;
+        acc[4] += x1[j].x * f; acc[5] += x1[j].y * f; acc[6] += x1[j].z * f; acc[7] += x1[j].w * f;
+      }
     }
   }
   const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
@@ -864,6 +901,89 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
     o.z = pack_bf16x2(acc[4], acc[5]);
     o.w = pack_bf16x2(acc[6], acc[7]);
     *reinterpret_cast<uint4*>(a.out + (int64_t)r * D + 8 * sub) = o;
+  }
+}
+
+// The same merge for many splits: one block per output row.  Slice k of the
+// block (LPR lanes) merges splits k, k + NSL, ... into (m_k, l_k, acc_k); the
+// slices then meet in LDS and the first LPR lanes finish the row.
+template <int D>
+__global__ __launch_bounds__(256) void decode_attn_combine_wide_kernel(AttnArgs a) {
+  constexpr int LPR = D / 8, NSL = 256 / LPR;
+  __shared__ float s_acc[NSL][D];
+  __shared__ float s_ml[NSL][2];
+  const int sub = threadIdx.x % LPR, k = threadIdx.x / LPR;
+  const int r = blockIdx.x;
+  const float* part = a.part + (int64_t)r * a.splits * part_stride<D>();
+  float mm = -INFINITY;
+  for (int s = k; s < a.splits; s += NSL) mm = fmaxf(mm, part[s * part_stride<D>() + D]);
+  float ll = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (mm != -INFINITY) {
+    for (int s = k; s < a.splits; s += NSL) {
+      const float* ps = part + s * part_stride<D>();
+      const float f = exp2f(ps[D] - mm);
+      ll += ps[D + 1] * f;
+      const float4 x0 = *reinterpret_cast<const float4*>(ps + 8 * sub);
+      const float4 x1 = *reinterpret_cast<const float4*>(ps + 8 * sub + 4);
+      acc[0] += x0.x * f; acc[1] += x0.y * f; acc[2] += x0.z * f; acc[3] += x0.w * f;
+      acc[4] += x1.x * f; acc[5] += x1.y * f; acc[6] += x1.z * f; acc[7] += x1.w * f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s_acc[k][8 * sub + i] = acc[i];
+  if (sub == 0) {
+    s_ml[k][0] = mm;
+    s_ml[k][1] = ll;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  // wave 0: every lane rebuilds row r (lanes >= LPR repeat lanes % LPR and store nothing)
+  float m_all = -INFINITY;
+  for (int j = 0; j < NSL; ++j) m_all = fmaxf(m_all, s_ml[j][0]);
+  float l_all = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (m_all != -INFINITY) {
+    for (int j = 0; j < NSL; ++j) {
+      const float f = exp2f(s_ml[j][0] - m_all);
+      l_all += s_ml[j][1] * f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += s_acc[j][8 * sub + i] * f;
+    }
+  }
+  const float inv = (l_all > 0.f) ? 1.f / l_all : 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] *= inv;
+  fwht_row<D>(acc, sub);
+  const float rd = inv_sqrt_d<D>();
+  const uint2 sw = *reinterpret_cast<const uint2*>(a.signs + 8 * sub);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int8_t sb = (int8_t)((i < 4 ? sw.x : sw.y) >> (8 * (i & 3)));
+    acc[i] = (l_all > 0.f) ? acc[i] * rd * (sb < 0 ? -1.f : 1.f) : 0.f;
+  }
+  if ((int)threadIdx.x < LPR) {
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(a.out + (int64_t)r * D + 8 * sub) = o;
+  }
+}
+
+// Merge kernel choice: the per-row kernel reads a row's splits serially, the
+// wide one spreads them over a block (worth it once there are many splits).
+template <int D>
+static void launch_combine(const AttnArgs& a, hipStream_t st) {
+  const int rows = a.batch * a.n_queries * a.n_q_heads;
+  if (a.splits >= 16) {
+    decode_attn_combine_wide_kernel<D><<<dim3((unsigned)rows), 256, 0, st>>>(a);
+  } else {
+    const int rows_per_block = 4 * (64 / (D / 8));
+    decode_attn_combine_kernel<D><<<dim3((rows + rows_per_block - 1) / rows_per_block), 256, 0, st>>>(a);
   }
 }
 
@@ -924,9 +1044,7 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
         case 4: decode_attn_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(a); break;
         default: decode_attn_mfma_kernel<D, 5><<<grid, 256, 0, st>>>(a); break;
       }
-      const int rows = a.batch * a.n_queries * a.n_q_heads;
-      const int rows_per_block = 4 * (64 / (D / 8));
-      decode_attn_combine_kernel<D><<<dim3((rows + rows_per_block - 1) / rows_per_block), 256, 0, st>>>(a);
+      launch_combine<D>(a, st);
       return hipGetLastError();
     }
   }
@@ -936,9 +1054,7 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
     case 5: launch_split_kb<D, 5>(a, vb, grid, st); break;
     default: launch_split_kb<D, 8>(a, vb, grid, st); break;
   }
-  const int rows = a.batch * a.n_queries * a.n_q_heads;
-  const int rows_per_block = 4 * (64 / (D / 8));
-  decode_attn_combine_kernel<D><<<dim3((rows + rows_per_block - 1) / rows_per_block), 256, 0, st>>>(a);
+  launch_combine<D>(a, st);
   return hipGetLastError();
 }
 
