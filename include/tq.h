@@ -250,7 +250,8 @@ int32_t tq_attn_quant(const tq_scheme* scheme, const uint16_t* q_bf16, int32_t b
  * float32 sums of exact bf16 products; float32 operands (residual,
  * reconstruction) enter as bf16 hi + lo pairs.  Served: d in {64, 128, 256},
  * bits in {1, 2, 3, 4}, qjl only for d <= 128 (the matrices stay resident in
- * one compute unit's LDS).  Inputs are finite, with ||x||^2 inside float32.
+ * one compute unit's LDS).  Inputs are finite, and a row is zero or has
+ * ||x||^2 in the normal float32 range [2^-126, 2^128).
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t head_dim;

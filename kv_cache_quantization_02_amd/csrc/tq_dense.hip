@@ -20,15 +20,13 @@
 // block copies it once into LDS in fragment order (fragment (t, k) is 1 KB,
 // lane l's 16 bytes at 16 l, so every A read is one conflict-free
 // ds_read_b128).  Rows of the batch are the 16 columns of the B operand and
-// of the result.  Output coordinate o and contraction index are permuted so
-// that lane-group g = l/16 owns the W = d/4 consecutive coordinates
-// [W g, W g + W) of its row on both sides of every product:
-//   result row m of output tile t   <->  coordinate W (m/4) + 4 t + m%4
-//   contraction slot 8 g + e of chunk k  <->  coordinate W g + 8 k + e
-// so a lane's results are its next product's B operand without any exchange,
-// its bf16 input load is 2W contiguous bytes, its code bits are one
-// contiguous piece of the row's bitstream, and per-row sums need only the
-// four lane-groups (two permlane swaps).
+// of the result.  Output coordinates and contraction indices are permuted
+// (the coordinate maps below) so that lane-group g = l/16 of a row holds the
+// coordinates 32 q + 8 g + [0, 8) on both sides of every product: a lane's
+// results are its next product's B operand without any exchange, loads and
+// code stores are contiguous per row, and per-row sums need only the four
+// lane-groups.  The dequantizer's last product takes the data as the A
+// operand, so that its results spread over the lanes by rows.
 //
 // Exactness: bf16 rows and bf16 matrices make every MFMA product exact; sums
 // are float32.  Operands that are float32 (the residual, the reconstruction)
@@ -72,7 +70,7 @@ struct DenseCfg {
   static constexpr int W = D / 4;      // coordinates per lane and row
   static constexpr int NT = D / 16;    // result tiles of 16 coordinates
   static constexpr int NK = D / 32;    // contraction chunks of 32
-  static constexpr int NC = D == 64 ? 4 : 2;  // 16-row column tiles per wave
+  static constexpr int NC = 2;         // 16-row column tiles per wave
   static constexpr int RW = 16 * NC;   // rows per wave and step
   static constexpr int MAT = D * D * 2;  // bytes of one matrix in LDS
 };
@@ -89,58 +87,40 @@ __device__ __forceinline__ uint32_t dn_pack_bf16(float lo, float hi) { return pa
 
 // Coordinate maps.  Result row m of output tile t, and contraction slot
 // 8 gp + e of chunk kc (gp = l/16 of the lane holding it), stand for:
-//   kBlocked:     lane-group g owns [W g, W g + W):
-//       out(t, m) = W (m/4) + 4 t + m%4,     in(kc, gp, e) = W gp + 8 kc + e
 //   kInterleaved: lane-group g owns 32 q + 8 g + [0, 8) for every q:
 //       out(t, m) = 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4,   in(kc, gp, e) = 32 kc + 8 gp + e
 //   kRows (output only, for the product whose data is the A operand):
 //       out(t, n) = NT n + t, so lane n holds NT consecutive coordinates of
 //       four data rows
-// With the first two a lane's result j = 4 t + e is its B operand element
-// j = 8 kc + e of the next product.  The quantizer uses kBlocked (a lane's
-// code bits are one piece of the bitstream); the dequantizer reads its codes
-// in the kInterleaved order and writes its rows through kRows, so that every
-// store instruction covers whole rows.
-enum { kBlocked = 0, kInterleaved = 1, kRows = 2 };
+// With kInterleaved a lane's result j = 4 t + e is its B operand element
+// j = 8 kc + e of the next product, so products chain without any exchange;
+// the four lane-groups of a row load 64 contiguous bytes per instruction; and
+// a lane's 8 codes of chunk q are one B-byte piece of the row's bitstream.
+// The dequantizer writes its rows through kRows, so that every store
+// instruction covers whole rows.
+enum { kInterleaved = 1, kRows = 2 };
 
 template <int D, int MAP>
 __device__ __forceinline__ int dn_out_coord(int t, int m) {
   if constexpr (MAP == kInterleaved) return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
-  else if constexpr (MAP == kRows) return (D / 16) * m + t;
-  else return (D / 4) * (m >> 2) + 4 * t + (m & 3);
+  else return (D / 16) * m + t;
 }
-template <int D, int MAP>
-__device__ __forceinline__ int dn_in_coord(int kc, int gp) {
-  if constexpr (MAP == kInterleaved) return 32 * kc + 8 * gp;
-  else return (D / 4) * gp + 8 * kc;
-}
+__device__ __forceinline__ int dn_in_coord(int kc, int gp) { return 32 * kc + 8 * gp; }
 template <int D, int MAP>
 __device__ __forceinline__ void dn_out_slot(int o, int& t, int& m) {
   if constexpr (MAP == kInterleaved) {
     const int r = o & 31;
     t = 2 * (o >> 5) + ((r & 7) >> 2);
     m = 4 * (r >> 3) + (r & 3);
-  } else if constexpr (MAP == kRows) {
+  } else {
     t = o % (D / 16);
     m = o / (D / 16);
-  } else {
-    const int j = o % (D / 4);
-    t = j >> 2;
-    m = 4 * (o / (D / 4)) + (j & 3);
   }
 }
-template <int D, int MAP>
 __device__ __forceinline__ void dn_in_slot(int in, int& kc, int& gp, int& e) {
-  if constexpr (MAP == kInterleaved) {
-    kc = in >> 5;
-    gp = (in >> 3) & 3;
-    e = in & 7;
-  } else {
-    const int j = in % (D / 4);
-    gp = in / (D / 4);
-    kc = j >> 3;
-    e = j & 7;
-  }
+  kc = in >> 5;
+  gp = (in >> 3) & 3;
+  e = in & 7;
 }
 
 // Copy the d x d bf16 matrix M (row-major) into LDS in fragment order for
@@ -148,7 +128,7 @@ __device__ __forceinline__ void dn_in_slot(int in, int& kc, int& gp, int& e) {
 // l holds the 8 elements (out(t, l%16), in(kc, l/16, 0..7)); the same bytes
 // serve as the A operand (matrix rows = outputs) or, with the data as A, as
 // the B operand (matrix columns = outputs).
-template <int D, bool TRANSPOSE, int OUT, int IN>
+template <int D, bool TRANSPOSE, int OUT>
 __device__ __forceinline__ void dn_load_matrix(uint8_t* lds, const uint16_t* __restrict__ m) {
   using C = DenseCfg<D>;
   constexpr int NK = C::NK;
@@ -157,7 +137,7 @@ __device__ __forceinline__ void dn_load_matrix(uint8_t* lds, const uint16_t* __r
       const int f = p >> 6, l = p & 63;
       const int t = f / NK, kc = f % NK;
       const int o = dn_out_coord<D, OUT>(t, l & 15);
-      const int in0 = dn_in_coord<D, IN>(kc, l >> 4);
+      const int in0 = dn_in_coord(kc, l >> 4);
       const dn_u32x4 v = *reinterpret_cast<const dn_u32x4*>(m + o * D + in0);
       *(dn_lds_u32x4*)(lds + 16 * p) = v;
     }
@@ -168,7 +148,7 @@ __device__ __forceinline__ void dn_load_matrix(uint8_t* lds, const uint16_t* __r
       const int a = p / (D / 8), b0 = (p % (D / 8)) * 8;
       const dn_u32x4 v = *reinterpret_cast<const dn_u32x4*>(m + a * D + b0);
       int kc, gp, e;
-      dn_in_slot<D, IN>(a, kc, gp, e);
+      dn_in_slot(a, kc, gp, e);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         int t, mrow;
@@ -187,13 +167,17 @@ __device__ __forceinline__ dn_bf16x8 dn_frag(const uint8_t* lds, int f, int lane
 
 __device__ __forceinline__ dn_bf16x8 dn_bits(dn_u32x4 v) { return __builtin_bit_cast(dn_bf16x8, v); }
 
-// acc[c][t] += M x over all chunks, M's fragments in LDS, x the B operands.
+// acc[c][t] += M x over all chunks, M's fragments in LDS, x the B operands
+// (NX = 2: x = hi + lo, both contracted against each fragment read once).
 // The fragments of tile t+1 are read while tile t's products run; the
 // scheduling barrier keeps the compiler from hoisting further reads (which
-// would hold every fragment of the matrix in registers).
-template <int D>
+// would hold every fragment of the matrix in registers).  ROWS swaps the
+// operands: the data is A, so lane (n, g) receives rows 16 c + 4 g + i
+// (i = 0..3) of the batch at output coordinate out(t, n).
+template <int D, int NX, bool ROWS = false>
 __device__ __forceinline__ void dn_gemm(dn_f32x4 (&acc)[DenseCfg<D>::NC][DenseCfg<D>::NT], const uint8_t* lds,
-                                        const dn_u32x4 (&bx)[DenseCfg<D>::NC][DenseCfg<D>::NK], int lane) {
+                                        const dn_u32x4 (&b0)[DenseCfg<D>::NC][DenseCfg<D>::NK],
+                                        const dn_u32x4 (&b1)[DenseCfg<D>::NC][DenseCfg<D>::NK], int lane) {
   using C = DenseCfg<D>;
   dn_bf16x8 cur[C::NK], nxt[C::NK];
 #pragma unroll
@@ -207,35 +191,17 @@ __device__ __forceinline__ void dn_gemm(dn_f32x4 (&acc)[DenseCfg<D>::NC][DenseCf
 #pragma unroll
     for (int kc = 0; kc < C::NK; ++kc) {
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[kc], dn_bits(bx[c][kc]), acc[c][t], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kc = 0; kc < C::NK; ++kc) cur[kc] = nxt[kc];
-  }
-}
-
-// acc[c][t] += x M^T with the data as the A operand: lane (n, g) receives
-// rows 16 c + 4 g + i (i = 0..3) of the batch at output coordinate out(t, n).
-template <int D>
-__device__ __forceinline__ void dn_gemm_rows(dn_f32x4 (&acc)[DenseCfg<D>::NC][DenseCfg<D>::NT], const uint8_t* lds,
-                                             const dn_u32x4 (&bx)[DenseCfg<D>::NC][DenseCfg<D>::NK], int lane) {
-  using C = DenseCfg<D>;
-  dn_bf16x8 cur[C::NK], nxt[C::NK];
-#pragma unroll
-  for (int kc = 0; kc < C::NK; ++kc) cur[kc] = dn_frag(lds, kc, lane);
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-    if (t + 1 < C::NT) {
-#pragma unroll
-      for (int kc = 0; kc < C::NK; ++kc) nxt[kc] = dn_frag(lds, (t + 1) * C::NK + kc, lane);
-    }
-#pragma unroll
-    for (int kc = 0; kc < C::NK; ++kc) {
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dn_bits(bx[c][kc]), cur[kc], acc[c][t], 0, 0, 0);
+      for (int c = 0; c < C::NC; ++c) {
+        if constexpr (ROWS) {
+          acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dn_bits(b0[c][kc]), cur[kc], acc[c][t], 0, 0, 0);
+          if constexpr (NX == 2)
+            acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dn_bits(b1[c][kc]), cur[kc], acc[c][t], 0, 0, 0);
+        } else {
+          acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[kc], dn_bits(b0[c][kc]), acc[c][t], 0, 0, 0);
+          if constexpr (NX == 2)
+            acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[kc], dn_bits(b1[c][kc]), acc[c][t], 0, 0, 0);
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -266,42 +232,38 @@ __device__ __forceinline__ void dn_split(const dn_f32x4 (&v)[DenseCfg<D>::NC][De
   }
 }
 
-// Bytes of a lane's piece of the index plane row, and of the QJL plane row.
-template <int D, int B>
-struct DenseSeg {
-  static constexpr int BITS = DenseCfg<D>::W * B;
-  static constexpr int BYTES = BITS / 8;
-  static constexpr int WORDS = (BYTES + 3) / 4;
-};
-
-template <int BYTES, int WORDS>
-__device__ __forceinline__ void dn_store_seg(uint8_t* p, const uint32_t (&w)[WORDS]) {
-  if constexpr (BYTES % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < BYTES / 4; ++i) reinterpret_cast<uint32_t*>(p)[i] = w[i];
+// Magnitude part of the Lloyd-Max index: m = HALF + #{thr_j < a} for the
+// 2^(B-1) - 1 ascending positive thresholds, by a branch-free binary search
+// (one compare per level).
+template <int B>
+__device__ __forceinline__ void dn_search(const float* thr, float ay, uint32_t& m) {
+  constexpr uint32_t HALF = 1u << (B - 1);
+  if constexpr (B == 1) {
+    m = HALF;
+  } else if constexpr (B == 2) {
+    m = HALF + (thr[0] < ay ? 1u : 0u);
+  } else if constexpr (B == 3) {
+    const bool c1 = thr[1] < ay;
+    const bool c2 = (c1 ? thr[2] : thr[0]) < ay;
+    m = (c1 ? HALF + 2u : HALF) + (c2 ? 1u : 0u);
   } else {
-#pragma unroll
-    for (int i = 0; i < BYTES / 2; ++i) reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+    const bool c1 = thr[3] < ay;
+    const bool c2 = (c1 ? thr[5] : thr[1]) < ay;
+    const float ta = c1 ? thr[4] : thr[0], tb = c1 ? thr[6] : thr[2];
+    const bool c3 = (c2 ? tb : ta) < ay;
+    m = (c1 ? HALF + 4u : HALF) + (c2 ? 2u : 0u) + (c3 ? 1u : 0u);
   }
-}
-
-template <int B, int WORDS>
-__device__ __forceinline__ void dn_put_field(uint32_t (&w)[WORDS], int j, uint32_t v) {
-  const int bit = B * j, wi = bit >> 5, sh = bit & 31;
-  w[wi] |= v << sh;
-  if (sh + B > 32) w[wi + 1] |= v >> (32 - sh);
 }
 
 // ------------------------------------------------------------- quantize
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
   using C = DenseCfg<D>;
-  using Seg = DenseSeg<D, B>;
-  constexpr int W = C::W, NT = C::NT, NK = C::NK, NC = C::NC;
+  constexpr int NT = C::NT, NK = C::NK, NC = C::NC;
   constexpr int HALF = 1 << (B - 1), NP = HALF - 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::MAT * (QJL ? 2 : 1)];
-  dn_load_matrix<D, false, kBlocked, kBlocked>(lds, a.rot);
-  if constexpr (QJL) dn_load_matrix<D, false, kBlocked, kBlocked>(lds + C::MAT, a.proj);
+  dn_load_matrix<D, false, kInterleaved>(lds, a.rot);
+  if constexpr (QJL) dn_load_matrix<D, false, kInterleaved>(lds + C::MAT, a.proj);
   __syncthreads();
 
   const int lane = (int)__lane_id();
@@ -315,60 +277,41 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
   for (int j = 0; j < HALF; ++j) pcen[j] = __uint_as_float(dn_centroids<B>()[HALF + j]);
   const float rsd = inv_sqrt_d<D>();
 
-  // the rows of a tile: B operands (bf16 x), plane row index, liveness
-  dn_u32x4 bx[NC][NK];
-  int64_t po[NC];
-  bool act[NC];
-  auto load_tile = [&](uint32_t tile) {
+  // the rows of a tile: B operands (bf16 x), plane row index, liveness; the
+  // next tile's rows load into the second set while this one is worked on
+  dn_u32x4 bx[NC][NK], bn[NC][NK];
+  int64_t po[NC], pn[NC];
+  bool act[NC], an[NC];
+  auto load_tile = [&](uint32_t tile, dn_u32x4 (&dst)[NC][NK], int64_t (&pdst)[NC], bool (&adst)[NC]) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint32_t r = tile * C::RW + 16 * c + n;
-      act[c] = r < a.rows;
+      adst[c] = r < a.rows;
       uint32_t s, t, h;
-      split_row(act[c] ? r : 0u, a.split, s, t, h);
+      split_row(adst[c] ? r : 0u, a.split, s, t, h);
       const int64_t xo = row_index(a.x_map, s, t, h);
-      po[c] = row_index(a.plane_map, s, t, h);
-      const dn_u32x4* src = reinterpret_cast<const dn_u32x4*>(a.x + xo * D + W * g);
+      pdst[c] = row_index(a.plane_map, s, t, h);
+      // chunk kc: coordinates 32 kc + 8 g + [0, 8), so the four lane-groups
+      // of a row read 64 contiguous bytes per instruction
+      const uint16_t* src = a.x + xo * D + 8 * g;
 #pragma unroll
-      for (int kc = 0; kc < NK; ++kc) bx[c][kc] = act[c] ? src[kc] : dn_u32x4{0u, 0u, 0u, 0u};
+      for (int kc = 0; kc < NK; ++kc)
+        dst[c][kc] = adst[c] ? *reinterpret_cast<const dn_u32x4*>(src + 32 * kc) : dn_u32x4{0u, 0u, 0u, 0u};
     }
   };
-  // code words of a zero row: every index is #{b < 0} = HALF - 1
-  uint32_t zseg[Seg::WORDS];
+  // an 8-coordinate piece of a zero row: every index is #{b < 0} = HALF - 1
+  uint32_t zpiece = 0u;
 #pragma unroll
-  for (int i = 0; i < Seg::WORDS; ++i) zseg[i] = 0u;
-#pragma unroll
-  for (int j = 0; j < W; ++j) dn_put_field<B>(zseg, j, (uint32_t)(HALF - 1));
+  for (int e = 0; e < 8; ++e) zpiece |= (uint32_t)(HALF - 1) << (B * e);
 
   uint32_t tile = blockIdx.x * 4u + wave;
   if (tile * (uint32_t)C::RW >= a.rows) return;
-  load_tile(tile);
+  load_tile(tile, bx, po, act);
   for (;;) {
-    // norms
-    float nrm[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float ss = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < NK; ++kc) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float v0 = bf16_lo(bx[c][kc][w]), v1 = bf16_hi(bx[c][kc][w]);
-          ss = __builtin_fmaf(v0, v0, ss);
-          ss = __builtin_fmaf(v1, v1, ss);
-        }
-      }
-      nrm[c] = __builtin_sqrtf(dn_sum_groups(ss));
-    }
-    // y = P x
-    dn_f32x4 acc[NC][NT];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
-    dn_gemm<D>(acc, lds, bx, lane);
-
-    // the next tile's rows load while this one is coded
+    // the next tile's rows: loaded now into the second set (MSE), or into the
+    // first once the rotation has consumed it (QJL, which needs the registers)
+    const uint32_t next = tile + gridDim.x * 4u;
+    const bool more = next * (uint32_t)C::RW < a.rows;
     int64_t pc[NC];
     bool ac[NC];
 #pragma unroll
@@ -376,59 +319,134 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
       pc[c] = po[c];
       ac[c] = act[c];
     }
-    const uint32_t next = tile + gridDim.x * 4u;
-    const bool more = next * (uint32_t)C::RW < a.rows;
-    if (more) load_tile(next);
+    if constexpr (!QJL) {
+      if (more) load_tile(next, bn, pn, an);
+    }
 
-    float gam[NC];
+    // norms: the Gram matrix X X^T of each 16-row column tile on the matrix
+    // cores (the B registers serve as both operands: exact products, float32
+    // sums); row n's squared norm is its diagonal entry, held by lane
+    // (n, n/4) as element n%4, and fetched by every lane of the row
+    float nrm[NC], sc[NC], thr[NC][NP > 0 ? NP : 1];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      dn_f32x4 gram = dn_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc)
+        gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dn_bits(bx[c][kc]), dn_bits(bx[c][kc]), gram, 0, 0, 0);
+      const float g01 = (n & 1) ? gram[1] : gram[0];
+      const float g23 = (n & 1) ? gram[3] : gram[2];
+      const float diag = (n & 2) ? g23 : g01;
+      const int holder = 16 * (n >> 2) + n;
+      const float ss = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * holder, __float_as_int(diag)));
+      nrm[c] = __builtin_sqrtf(ss);
       // u > b  <=>  |y| > b * norm / sqrt(d) on the side of y's sign
-      const float sc = nrm[c] * rsd;
-      float thr[NP > 0 ? NP : 1];
+      sc[c] = nrm[c] * rsd;
 #pragma unroll
-      for (int j = 0; j < NP; ++j) thr[j] = pbnd[j] * sc;
-      uint32_t seg[Seg::WORDS];
+      for (int j = 0; j < NP; ++j) thr[c][j] = pbnd[j] * sc[c];
+    }
+
+    // y = P x, each output tile coded while the next one's products run (MSE).
+    // piece[c][q]: the 8 B-bit codes of coordinates 32 q + 8 g + [0, 8) of
+    // row 16 c + n, stream bytes B (4 q + g) .. of the row
+    dn_f32x4 acc[NC][NT];
 #pragma unroll
-      for (int i = 0; i < Seg::WORDS; ++i) seg[i] = 0u;
-      float gg = 0.f;
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+      for (int t = 0; t < NT; ++t) acc[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
+    uint32_t piece[NC][NK];
+    float gg[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      gg[c] = 0.f;
+#pragma unroll
+      for (int q = 0; q < NK; ++q) piece[c][q] = 0u;
+    }
+    auto code_tile = [&](int t) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float y = acc[c][t][e];
           const float ay = __builtin_fabsf(y);
           uint32_t m = HALF;
           float mag = pcen[0];
+          if constexpr (QJL) {
+            // a linear scan yields the cell's centroid with one select per
+            // threshold (and fewer live registers than the search's muxes)
 #pragma unroll
-          for (int j = 0; j < NP; ++j) {
-            const bool above = thr[j] < ay;
-            m += above ? 1u : 0u;
-            if constexpr (QJL) mag = above ? pcen[j + 1] : mag;
+            for (int j = 0; j < NP; ++j) {
+              const bool above = thr[c][j] < ay;
+              m += above ? 1u : 0u;
+              mag = above ? pcen[j + 1] : mag;
+              // keep the select chain (the compiler would otherwise index
+              // the table with the count, through scratch memory)
+              asm volatile("" : "+v"(mag));
+            }
+          } else {
+            dn_search<B>(thr[c], ay, m);
           }
           // #{b < u} = HALF + m for y > 0 and HALF - 1 - m = (HALF + m) ^ (2 HALF - 1)
           // for y < 0; all ones where the sign bit is set (y = +0 lies on the
           // middle boundary 0, a tie either way; a zero row is set below)
           const uint32_t neg = (uint32_t)(__float_as_int(y) >> 31);
           const uint32_t idx = m ^ (neg & (uint32_t)(2 * HALF - 1));
-          dn_put_field<B>(seg, 4 * t + e, idx);
+          piece[c][t >> 1] |= idx << (B * (4 * (t & 1) + e));
           if constexpr (QJL) {
             const float yh = __uint_as_float(__float_as_uint(mag) ^ (neg & 0x80000000u));
-            const float rho = __builtin_fmaf(-yh, sc, y);
+            const float rho = __builtin_fmaf(-yh, sc[c], y);
             acc[c][t][e] = rho;
-            gg = __builtin_fmaf(rho, rho, gg);
+            gg[c] = __builtin_fmaf(rho, rho, gg[c]);
           }
         }
       }
+    };
+    if constexpr (QJL) {
+      // (the QJL stage needs the registers: product first, then coding)
+      dn_gemm<D, 1>(acc, lds, bx, bx, lane);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) code_tile(t);
+    } else {
+      dn_bf16x8 cur[NK], nxt[NK];
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) cur[kc] = dn_frag(lds, kc, lane);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t + 1 < NT) {
+#pragma unroll
+          for (int kc = 0; kc < NK; ++kc) nxt[kc] = dn_frag(lds, (t + 1) * NK + kc, lane);
+        }
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[kc], dn_bits(bx[c][kc]), acc[c][t], 0, 0, 0);
+        }
+        if (t > 0) code_tile(t - 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) cur[kc] = nxt[kc];
+      }
+      code_tile(NT - 1);
+    }
+    if constexpr (QJL) {
+      if (more) load_tile(next, bx, po, act);
+    }
+
+    float gam[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
       if (nrm[c] == 0.f) {
 #pragma unroll
-        for (int i = 0; i < Seg::WORDS; ++i) seg[i] = zseg[i];
+        for (int q = 0; q < NK; ++q) piece[c][q] = zpiece;
       }
       if (ac[c]) {
-        dn_store_seg<Seg::BYTES>(a.idx + pc[c] * (D * B / 8) + g * Seg::BYTES, seg);
+        uint8_t* irow = a.idx + pc[c] * (D * B / 8);
+#pragma unroll
+        for (int q = 0; q < NK; ++q) store_lane_bits<B>(irow, 4 * q + g, piece[c][q]);
         if (g == 0) a.norm[pc[c]] = nrm[c];
       }
-      if constexpr (QJL) gam[c] = __builtin_sqrtf(dn_sum_groups(gg));
+      if constexpr (QJL) gam[c] = __builtin_sqrtf(dn_sum_groups(gg[c]));
     }
 
     if constexpr (QJL) {
@@ -439,24 +457,59 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int t = 0; t < NT; ++t) sp[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
-      dn_gemm<D>(sp, lds + C::MAT, hi, lane);
-      dn_gemm<D>(sp, lds + C::MAT, lo, lane);
+      dn_gemm<D, 2>(sp, lds + C::MAT, hi, lo, lane);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        uint32_t qb[1] = {0u};
+        // sign bits of coordinates 32 q + 8 g + [0, 8): byte 4 q + g of the row
+        uint32_t qb[NK];
+#pragma unroll
+        for (int q = 0; q < NK; ++q) qb[q] = 0u;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qb[0] |= (sp[c][t][e] >= 0.f ? 1u : 0u) << (4 * t + e);
+          for (int e = 0; e < 4; ++e) qb[t >> 1] |= (sp[c][t][e] >= 0.f ? 1u : 0u) << (4 * (t & 1) + e);
         if (ac[c]) {
-          dn_store_seg<W / 8>(a.qjl + pc[c] * (D / 8) + g * (W / 8), qb);
+          uint8_t* qrow = a.qjl + pc[c] * (D / 8);
+#pragma unroll
+          for (int q = 0; q < NK; ++q) store_lane_bits<1>(qrow, 4 * q + g, qb[q]);
           if (g == 0) a.gamma[pc[c]] = gam[c];
         }
       }
     }
     if (!more) break;
     tile = next;
+    if constexpr (!QJL) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        po[c] = pn[c];
+        act[c] = an[c];
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) bx[c][kc] = bn[c][kc];
+      }
+    }
   }
+}
+
+// A lane's 8-code piece of a packed row: B bytes at byte offset B * sub,
+// read as the aligned dword(s) that hold it (the second one clamped into the
+// row; rows are multiples of 8 bytes) and combined only when used, so that
+// prefetched pieces stay in flight until then.
+template <int B>
+__device__ __forceinline__ void dn_piece_load(const uint8_t* row, int sub, int row_bytes, uint32_t& w0, uint32_t& w1) {
+  const int a = (B * sub) & ~3;
+  w0 = *reinterpret_cast<const uint32_t*>(row + a);
+  if constexpr (B == 3) {
+    const int a1 = (a + 4 < row_bytes - 4) ? a + 4 : row_bytes - 4;
+    w1 = *reinterpret_cast<const uint32_t*>(row + a1);
+  } else {
+    w1 = 0u;
+  }
+}
+template <int B>
+__device__ __forceinline__ uint32_t dn_piece_bits(uint32_t w0, uint32_t w1, int sub) {
+  const uint32_t sh = (uint32_t)((B * sub) & 3) * 8u;
+  if constexpr (B == 3) return __builtin_amdgcn_alignbit(w1, w0, sh);
+  else return w0 >> sh;
 }
 
 // An output element: MSE sums finite centroid products, so the (canonical)
@@ -477,8 +530,8 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::MAT * (QJL ? 2 : 1)];
   // MSE: centroid as its bf16 hi (low half) and lo (high half); QJL: float32
   __shared__ uint32_t lut[1 << B];
-  dn_load_matrix<D, true, kRows, kInterleaved>(lds, a.rot);
-  if constexpr (QJL) dn_load_matrix<D, true, kInterleaved, kInterleaved>(lds + C::MAT, a.proj);
+  dn_load_matrix<D, true, kRows>(lds, a.rot);
+  if constexpr (QJL) dn_load_matrix<D, true, kInterleaved>(lds + C::MAT, a.proj);
   if (threadIdx.x < (1u << B)) {
     const float cv = __uint_as_float(dn_centroids<B>()[threadIdx.x]);
     if constexpr (QJL) {
@@ -497,10 +550,11 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
   const float rsd = inv_sqrt_d<D>();
   constexpr float kQjl = (float)(1.2533141373155002512 / D);  // sqrt(pi/2) / d
 
-  // fb[c][kc]: the 8 code fields of local elements 8 kc .. 8 kc + 7 of row
-  // 16 c + n, i.e. of coordinates 32 kc + 8 g + [0, 8): stream bytes
-  // B (4 kc + g) ..; qb the matching 8 sign bits, byte 4 kc + g of the QJL row
-  uint32_t fb[NC][NK], qb[NC][NK];
+  // Raw plane words of a tile, as loaded: (fw0, fw1)[c][kc] hold the 8 code
+  // fields of local elements 8 kc .. 8 kc + 7 of row 16 c + n, i.e. of
+  // coordinates 32 kc + 8 g + [0, 8) (stream bytes B (4 kc + g) ..); qw the
+  // word holding their 8 sign bits (byte 4 kc + g of the QJL row).
+  uint32_t fw0[NC][NK], fw1[NC][NK], qw[NC][NK];
   float sc[NC], cg[NC];
   int64_t xo[NC];
   auto load_tile = [&](uint32_t tile) {
@@ -515,26 +569,28 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
       if (act) {
         const uint8_t* irow = a.idx + po * (D * B / 8);
 #pragma unroll
-        for (int kc = 0; kc < NK; ++kc) fb[c][kc] = (uint32_t)load_lane_bits<B>(irow, 4 * kc + g);
+        for (int kc = 0; kc < NK; ++kc) dn_piece_load<B>(irow, 4 * kc + g, D * B / 8, fw0[c][kc], fw1[c][kc]);
         sc[c] = a.norm[po];
         if constexpr (QJL) {
           const uint8_t* qrow = a.qjl + po * (D / 8);
+          uint32_t unused;
 #pragma unroll
-          for (int kc = 0; kc < NK; ++kc) qb[c][kc] = (uint32_t)load_lane_bits<1>(qrow, 4 * kc + g);
+          for (int kc = 0; kc < NK; ++kc) dn_piece_load<1>(qrow, 4 * kc + g, D / 8, qw[c][kc], unused);
           cg[c] = a.gamma[po];
         }
       } else {
 #pragma unroll
-        for (int kc = 0; kc < NK; ++kc) fb[c][kc] = 0u;
+        for (int kc = 0; kc < NK; ++kc) fw0[c][kc] = fw1[c][kc] = 0u;
         sc[c] = 0.f;
         if constexpr (QJL) {
 #pragma unroll
-          for (int kc = 0; kc < NK; ++kc) qb[c][kc] = 0u;
+          for (int kc = 0; kc < NK; ++kc) qw[c][kc] = 0u;
           cg[c] = 0.f;
         }
       }
     }
   };
+  uint32_t fb[NC][NK], qb[NC][NK];
   auto field = [&](int c, int j) -> uint32_t {
     return __builtin_amdgcn_ubfe(fb[c][j >> 3], (uint32_t)(B * (j & 7)), (uint32_t)B);
   };
@@ -550,6 +606,11 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
     for (int c = 0; c < NC; ++c) {
       scale[c] = canon_nan(sc[c] * rsd);
       if constexpr (QJL) cg[c] = canon_nan(cg[c] * kQjl);
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) {
+        fb[c][kc] = dn_piece_bits<B>(fw0[c][kc], fw1[c][kc], 4 * kc + g);
+        if constexpr (QJL) qb[c][kc] = dn_piece_bits<1>(qw[c][kc], 0u, 4 * kc + g);
+      }
     }
     // A operands of the final product: bf16 hi and lo of y_hat (MSE: of the
     // centroids, the norm scale applied to the result)
@@ -589,7 +650,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int t = 0; t < NT; ++t) sq[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
-      dn_gemm<D>(sq, lds + C::MAT, bq, lane);
+      dn_gemm<D, 1>(sq, lds + C::MAT, bq, bq, lane);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -617,8 +678,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
-    dn_gemm_rows<D>(acc, lds, hi, lane);
-    dn_gemm_rows<D>(acc, lds, lo, lane);
+    dn_gemm<D, 2, true>(acc, lds, hi, lo, lane);
 
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -655,40 +715,52 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
   }
 }
 
-// Resident blocks: one per CU when a block's matrices take more than half
-// of the 160 KB LDS, else two; every block copies its matrices once.
-template <int D>
-unsigned dense_grid(uint32_t rows, bool qjl) {
-  using C = DenseCfg<D>;
-  const uint32_t tiles = (rows + C::RW - 1) / C::RW;
+// One round of resident blocks: the occupancy the compiled kernel allows (its
+// registers and LDS), times the compute units; every block copies its
+// matrices once and then loops over row tiles.
+template <int D, int B, bool QJL, bool DEQ>
+unsigned dense_grid(void (*kernel)(DenseArgs), uint32_t rows) {
+  constexpr int rows_per_wave = DenseCfg<D>::RW;
+  static int per_cu = 0, cus = 0;  // one pair per kernel
+  if (per_cu == 0) {
+    int occ = 0, dev = 0, n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ < 1) occ = 1;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 256;
+    cus = n;
+    per_cu = occ;
+  }
+  const uint32_t tiles = (rows + rows_per_wave - 1) / rows_per_wave;
   const unsigned want = (tiles + 3) / 4;
-  const unsigned per_cu = (C::MAT * (qjl ? 2 : 1) > 80 * 1024) ? 1u : 2u;
-  const unsigned cap = 256u * per_cu;
+  const unsigned cap = (unsigned)(cus * per_cu);
   return want < cap ? want : cap;
 }
 
 template <int D, int B>
 hipError_t dense_quant_db(const DenseArgs& a, bool qjl, hipStream_t st) {
-  const dim3 grid(dense_grid<D>(a.rows, qjl));
   if constexpr (D <= 128) {
     if (qjl) {
+      const dim3 grid(dense_grid<D, B, true, false>(dense_quantize_kernel<D, B, true>, a.rows));
       dense_quantize_kernel<D, B, true><<<grid, 256, 0, st>>>(a);
       return hipGetLastError();
     }
   }
+  const dim3 grid(dense_grid<D, B, false, false>(dense_quantize_kernel<D, B, false>, a.rows));
   dense_quantize_kernel<D, B, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
 template <int D, int B>
 hipError_t dense_dequant_db(const DenseArgs& a, bool qjl, hipStream_t st) {
-  const dim3 grid(dense_grid<D>(a.rows, qjl));
   if constexpr (D <= 128) {
     if (qjl) {
+      const dim3 grid(dense_grid<D, B, true, true>(dense_dequantize_kernel<D, B, true>, a.rows));
       dense_dequantize_kernel<D, B, true><<<grid, 256, 0, st>>>(a);
       return hipGetLastError();
     }
   }
+  const dim3 grid(dense_grid<D, B, false, true>(dense_dequantize_kernel<D, B, false>, a.rows));
   dense_dequantize_kernel<D, B, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }

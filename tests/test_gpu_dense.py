@@ -42,6 +42,8 @@ def _rows(n, d, seed):
         x[4] = 0.0
         x[4, 5] = -7.0                  # one spike
         x[5] = 1.0                      # constant row
+        x[6] *= 2.0 ** -60              # tiny (|x|^2 still a normal float32)
+        x[7] *= 2.0 ** 40               # huge
     return x.to(torch.bfloat16)
 
 
