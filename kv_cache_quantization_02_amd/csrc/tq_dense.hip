@@ -30,8 +30,8 @@
 //
 // Exactness: bf16 rows and bf16 matrices make every MFMA product exact; sums
 // are float32.  Operands that are float32 (the residual, the reconstruction)
-// are split into bf16 hi + lo and contracted twice, leaving a relative
-// operand error below 2^-16.
+// are split into bf16 hi + lo, both contracted against each matrix fragment
+// in the same pass, leaving a relative operand error below 2^-16.
 #include "tq_codebooks.h"
 #include "tq_launch.h"
 
@@ -67,7 +67,6 @@ __device__ __forceinline__ const uint32_t* dn_boundaries() {
 
 template <int D>
 struct DenseCfg {
-  static constexpr int W = D / 4;      // coordinates per lane and row
   static constexpr int NT = D / 16;    // result tiles of 16 coordinates
   static constexpr int NK = D / 32;    // contraction chunks of 32
   static constexpr int NC = 2;         // 16-row column tiles per wave
