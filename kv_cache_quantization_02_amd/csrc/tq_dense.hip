@@ -65,11 +65,17 @@ __device__ __forceinline__ const uint32_t* dn_boundaries() {
   else return kDnBnd4;
 }
 
+// NC: 16-row column tiles per wave.  The quantizer takes two (each matrix
+// fragment serves 32 rows).  The dequantizer takes one up to d = 128: fewer
+// live registers and more resident waves measured 8-9% faster there, while at
+// d = 256 the doubled fragment reads from LDS cost more than that.
 template <int D>
+constexpr int kDeqNC = D <= 128 ? 1 : 2;
+template <int D, int NCV>
 struct DenseCfg {
   static constexpr int NT = D / 16;    // result tiles of 16 coordinates
   static constexpr int NK = D / 32;    // contraction chunks of 32
-  static constexpr int NC = 2;         // 16-row column tiles per wave
+  static constexpr int NC = NCV;
   static constexpr int RW = 16 * NC;   // rows per wave and step
   static constexpr int MAT = D * D * 2;  // bytes of one matrix in LDS
 };
@@ -129,7 +135,7 @@ __device__ __forceinline__ void dn_in_slot(int in, int& kc, int& gp, int& e) {
 // the B operand (matrix columns = outputs).
 template <int D, bool TRANSPOSE, int OUT>
 __device__ __forceinline__ void dn_load_matrix(uint8_t* lds, const uint16_t* __restrict__ m) {
-  using C = DenseCfg<D>;
+  using C = DenseCfg<D, 1>;
   constexpr int NK = C::NK;
   if constexpr (!TRANSPOSE) {
     for (int p = threadIdx.x; p < C::NT * NK * 64; p += 256) {
@@ -173,11 +179,11 @@ __device__ __forceinline__ dn_bf16x8 dn_bits(dn_u32x4 v) { return __builtin_bit_
 // would hold every fragment of the matrix in registers).  ROWS swaps the
 // operands: the data is A, so lane (n, g) receives rows 16 c + 4 g + i
 // (i = 0..3) of the batch at output coordinate out(t, n).
-template <int D, int NX, bool ROWS = false>
-__device__ __forceinline__ void dn_gemm(dn_f32x4 (&acc)[DenseCfg<D>::NC][DenseCfg<D>::NT], const uint8_t* lds,
-                                        const dn_u32x4 (&b0)[DenseCfg<D>::NC][DenseCfg<D>::NK],
-                                        const dn_u32x4 (&b1)[DenseCfg<D>::NC][DenseCfg<D>::NK], int lane) {
-  using C = DenseCfg<D>;
+template <int D, int NC, int NX, bool ROWS = false>
+__device__ __forceinline__ void dn_gemm(dn_f32x4 (&acc)[NC][D / 16], const uint8_t* lds,
+                                        const dn_u32x4 (&b0)[NC][D / 32], const dn_u32x4 (&b1)[NC][D / 32],
+                                        int lane) {
+  using C = DenseCfg<D, NC>;
   dn_bf16x8 cur[C::NK], nxt[C::NK];
 #pragma unroll
   for (int kc = 0; kc < C::NK; ++kc) cur[kc] = dn_frag(lds, kc, lane);
@@ -210,11 +216,10 @@ __device__ __forceinline__ void dn_gemm(dn_f32x4 (&acc)[DenseCfg<D>::NC][DenseCf
 
 // Split float32 values (local coordinates j = 4t + e of acc) into bf16 hi
 // and lo B operands: chunk kc holds local coordinates 8kc .. 8kc+7.
-template <int D>
-__device__ __forceinline__ void dn_split(const dn_f32x4 (&v)[DenseCfg<D>::NC][DenseCfg<D>::NT],
-                                         dn_u32x4 (&hi)[DenseCfg<D>::NC][DenseCfg<D>::NK],
-                                         dn_u32x4 (&lo)[DenseCfg<D>::NC][DenseCfg<D>::NK]) {
-  using C = DenseCfg<D>;
+template <int D, int NC>
+__device__ __forceinline__ void dn_split(const dn_f32x4 (&v)[NC][D / 16], dn_u32x4 (&hi)[NC][D / 32],
+                                         dn_u32x4 (&lo)[NC][D / 32]) {
+  using C = DenseCfg<D, NC>;
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) {
 #pragma unroll
@@ -257,7 +262,7 @@ __device__ __forceinline__ void dn_search(const float* thr, float ay, uint32_t& 
 // ------------------------------------------------------------- quantize
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
-  using C = DenseCfg<D>;
+  using C = DenseCfg<D, 2>;
   constexpr int NT = C::NT, NK = C::NK, NC = C::NC;
   constexpr int HALF = 1 << (B - 1), NP = HALF - 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::MAT * (QJL ? 2 : 1)];
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
     };
     if constexpr (QJL) {
       // (the QJL stage needs the registers: product first, then coding)
-      dn_gemm<D, 1>(acc, lds, bx, bx, lane);
+      dn_gemm<D, NC, 1>(acc, lds, bx, bx, lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t) code_tile(t);
     } else {
@@ -450,13 +455,13 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
 
     if constexpr (QJL) {
       dn_u32x4 hi[NC][NK], lo[NC][NK];
-      dn_split<D>(acc, hi, lo);
+      dn_split<D, NC>(acc, hi, lo);
       dn_f32x4 sp[NC][NT];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int t = 0; t < NT; ++t) sp[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
-      dn_gemm<D, 2>(sp, lds + C::MAT, hi, lo, lane);
+      dn_gemm<D, NC, 2>(sp, lds + C::MAT, hi, lo, lane);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         // sign bits of coordinates 32 q + 8 g + [0, 8): byte 4 q + g of the row
@@ -523,7 +528,7 @@ __device__ __forceinline__ float dn_out(float v, float f) {
 // ----------------------------------------------------------- dequantize
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
-  using C = DenseCfg<D>;
+  using C = DenseCfg<D, kDeqNC<D>>;
   constexpr int NT = C::NT, NK = C::NK, NC = C::NC;
   // P^T for the final product (outputs in kRows order), S^T for the QJL term
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::MAT * (QJL ? 2 : 1)];
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int t = 0; t < NT; ++t) sq[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
-      dn_gemm<D, 1>(sq, lds + C::MAT, bq, bq, lane);
+      dn_gemm<D, NC, 1>(sq, lds + C::MAT, bq, bq, lane);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -659,7 +664,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
             const float cv = __uint_as_float(lut[field(c, 4 * t + e)]);
             sq[c][t][e] = __builtin_fmaf(cg[c], sq[c][t][e], cv * scale[c]);
           }
-      dn_split<D>(sq, hi, lo);
+      dn_split<D, NC>(sq, hi, lo);
     }
 
     // the next tile's planes load while this one is rebuilt
@@ -677,7 +682,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[c][t] = dn_f32x4{0.f, 0.f, 0.f, 0.f};
-    dn_gemm<D, 2, true>(acc, lds, hi, lo, lane);
+    dn_gemm<D, NC, 2, true>(acc, lds, hi, lo, lane);
 
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -719,7 +724,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
 // matrices once and then loops over row tiles.
 template <int D, int B, bool QJL, bool DEQ>
 unsigned dense_grid(void (*kernel)(DenseArgs), uint32_t rows) {
-  constexpr int rows_per_wave = DenseCfg<D>::RW;
+  constexpr int rows_per_wave = DenseCfg<D, DEQ ? kDeqNC<D> : 2>::RW;
   static int per_cu = 0, cus = 0;  // one pair per kernel
   if (per_cu == 0) {
     int occ = 0, dev = 0, n = 0;
