@@ -212,6 +212,31 @@ def measure_dense(tq, synth, k, v, dev):
     return out
 
 
+def measure_wide(tq, synth, dev):
+    """Timings of the codec at the other widths, outside the timed step: d256
+    k4v4 (48 layers x 4096 tokens x 4 kv-heads) and d512 k5v2 (48 x 1024 x 4)."""
+    import torch
+    out = {}
+    for wl in ("wide_k4v4_d256", "wide_k5v2_d512"):
+        rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS[wl]
+        k, v = synth.kv_inputs(rec, L, T, H, d, seed, device=dev)
+        sig = torch.from_numpy(synth.sign_vector(d)).to(dev)
+        planes = tq.alloc_planes(tq.scheme(d, kb, vb), (L, T, H), dev)
+        kout, vout = torch.empty_like(k), torch.empty_like(v)
+        us_q = _time_us(lambda: tq.quantize_kv(k, v, sig, kb, vb, out=planes), 10)
+        us_d = _time_us(lambda: tq.dequantize_kv(planes, sig, d, kb, vb, k_out=kout, v_out=vout), 10)
+        rows = L * T * H
+        nbytes = rows * (4 * d + tq.tq_row_bytes(tq.scheme(d, kb, vb)))
+        for name, us in (("quantize", us_q), ("dequantize", us_d)):
+            gbps = nbytes / (us * 1e-6) / 1e9
+            out[f"{name}_{wl}"] = {"workload": f"{L}x{T}x{H} rows, d={d}, k{kb}v{vb}",
+                                   "kernel": f"{name}_kernel<{d},{kb},{vb}>", "us": us,
+                                   "token_heads_per_s": rows / (us * 1e-6), "GBps": gbps,
+                                   "frac_of_hbm_peak": gbps / HBM_PEAK_GBS}
+        del k, v, planes, kout, vout
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,8 +312,12 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    phase_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-                for i, name in enumerate(("quantize", "dequantize", "decode_attn"))}
+    phase_runs = {name: sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+                  for i, name in enumerate(("quantize", "dequantize", "decode_attn"))}
+    phase_ms = {name: sum(r) / len(r) for name, r in phase_runs.items()}
+
+    def pct(r, q):  # nearest-rank percentile of a sorted list, in microseconds
+        return r[min(len(r) - 1, max(0, int(round(q * (len(r) - 1)))))] * 1e3
     _log(f"timed {args.steps} steps: {total_ms:.2f} ms GPU, {wall * 1e3:.2f} ms wall")
 
     row_bytes = tq.tq_row_bytes(sch)
@@ -307,8 +336,10 @@ def main():
                         "cache_token_heads_per_s": rows_a / (phase_ms["decode_attn"] * 1e-3),
                         "GBps": bytes_a / (phase_ms["decode_attn"] * 1e-3) / 1e9},
     }
-    for p in phases.values():
+    for name, p in phases.items():
         p["frac_of_hbm_peak"] = p["GBps"] / HBM_PEAK_GBS
+        r = phase_runs[name]
+        p["us_p10"], p["us_median"], p["us_p90"] = pct(r, 0.1), pct(r, 0.5), pct(r, 0.9)
     dom = max(phases, key=lambda n: phases[n]["us"])
     dom_bytes = {"quantize": bytes_q, "dequantize": bytes_dq, "decode_attn": bytes_a}[dom]
     kname = phases[dom]["kernel"].split("<")[0]
@@ -320,6 +351,7 @@ def main():
     if not args.no_next:
         next_rows = measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev)
         next_rows.update(measure_dense(tq, synth, k, v, dev))
+        next_rows.update(measure_wide(tq, synth, dev))
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
