@@ -325,118 +325,6 @@ __device__ __forceinline__ uint32_t lloyd_max_index(float yn, const float* lds_b
   }
 }
 
-// Lloyd-Max index bits of two elements ya, yb of a 2-, 3- or 4-bit table,
-// pushed into packed words.  Thresholds t[0] < ... < t[H-1] on |y|
-// (H = 2^(VB-1) - 1) give c = #{t < |y|} by binary search; the index is then
-// H + 1 + c for y > 0 and H - c otherwise, so its top bit is s = [y > 0] and
-// bit k below it is (bit k of c) XNOR s.  Each bit is a lane mask, and it
-// enters a word by w = 2 w + bit: one v_addc_co_u32 whose carry-in is the
-// mask.  Bits are pushed from the highest stream position down, ya's
-// (the higher element) first, so no bit is materialised, shifted or or-ed.
-// The first NH pushes go to word wh, the rest to wl (a pair of 3-bit
-// elements can straddle two words).
-//
-// Inline assembly because the compiler turns the plain-C form back into
-// select + shift + or.  Every vector read of a mask written by a vector
-// compare sits at least two instructions after it (the required wait
-// states), and all masks are internal to the block.
-#define TQ_PUSH(W, M) "v_addc_co_u32 %[" #W "], vcc, %[" #W "], %[" #W "], %[" #M "]\n\t"
-
-#define TQ_IDX2_BODY(W0, W1, W2, W3)                   \
-  "v_cmp_lt_f32_e64 %[rsa], 0, %[ya]\n\t"              \
-  "v_cmp_lt_f32_e64 %[rsb], 0, %[yb]\n\t"              \
-  "v_cmp_gt_f32_e64 %[r0a], |%[ya]|, %[t0]\n\t"        \
-  "v_cmp_gt_f32_e64 %[r0b], |%[yb]|, %[t0]\n\t"        \
-  "s_xnor_b64 %[r0a], %[r0a], %[rsa]\n\t"              \
-  "s_xnor_b64 %[r0b], %[r0b], %[rsb]\n\t"              \
-  TQ_PUSH(W0, rsa) TQ_PUSH(W1, r0a) TQ_PUSH(W2, rsb) TQ_PUSH(W3, r0b)
-
-#define TQ_IDX3_BODY(W0, W1, W2, W3, W4, W5)           \
-  "v_cmp_gt_f32_e64 %[r1a], |%[ya]|, %[t1]\n\t"        \
-  "v_cmp_gt_f32_e64 %[r1b], |%[yb]|, %[t1]\n\t"        \
-  "v_cmp_lt_f32_e64 %[rsa], 0, %[ya]\n\t"              \
-  "v_cndmask_b32_e64 %[ta], %[t0], %[t2], %[r1a]\n\t"  \
-  "v_cmp_lt_f32_e64 %[rsb], 0, %[yb]\n\t"              \
-  "v_cndmask_b32_e64 %[tb], %[t0], %[t2], %[r1b]\n\t"  \
-  "v_cmp_gt_f32_e64 %[r0a], |%[ya]|, %[ta]\n\t"        \
-  "v_cmp_gt_f32_e64 %[r0b], |%[yb]|, %[tb]\n\t"        \
-  "s_xnor_b64 %[r1a], %[r1a], %[rsa]\n\t"              \
-  "s_xnor_b64 %[r0a], %[r0a], %[rsa]\n\t"              \
-  "s_xnor_b64 %[r1b], %[r1b], %[rsb]\n\t"              \
-  "s_xnor_b64 %[r0b], %[r0b], %[rsb]\n\t"              \
-  TQ_PUSH(W0, rsa) TQ_PUSH(W1, r1a) TQ_PUSH(W2, r0a)   \
-  TQ_PUSH(W3, rsb) TQ_PUSH(W4, r1b) TQ_PUSH(W5, r0b)
-
-#define TQ_IDX4_BODY                                    \
-  "v_cmp_gt_f32_e64 %[r2a], |%[ya]|, %[t3]\n\t"        \
-  "v_cmp_gt_f32_e64 %[r2b], |%[yb]|, %[t3]\n\t"        \
-  "v_cmp_lt_f32_e64 %[rsa], 0, %[ya]\n\t"              \
-  "v_cndmask_b32_e64 %[ta], %[t1], %[t5], %[r2a]\n\t"  \
-  "v_cndmask_b32_e64 %[tb], %[t1], %[t5], %[r2b]\n\t"  \
-  "v_cndmask_b32_e64 %[ua], %[t0], %[t4], %[r2a]\n\t"  \
-  "v_cndmask_b32_e64 %[va], %[t2], %[t6], %[r2a]\n\t"  \
-  "v_cmp_gt_f32_e64 %[r1a], |%[ya]|, %[ta]\n\t"        \
-  "v_cndmask_b32_e64 %[ub], %[t0], %[t4], %[r2b]\n\t"  \
-  "v_cndmask_b32_e64 %[vb], %[t2], %[t6], %[r2b]\n\t"  \
-  "v_cmp_gt_f32_e64 %[r1b], |%[yb]|, %[tb]\n\t"        \
-  "v_cmp_lt_f32_e64 %[rsb], 0, %[yb]\n\t"              \
-  "v_cndmask_b32_e64 %[ta], %[ua], %[va], %[r1a]\n\t"  \
-  "v_cndmask_b32_e64 %[tb], %[ub], %[vb], %[r1b]\n\t"  \
-  "v_cmp_gt_f32_e64 %[r0a], |%[ya]|, %[ta]\n\t"        \
-  "v_cmp_gt_f32_e64 %[r0b], |%[yb]|, %[tb]\n\t"        \
-  "s_xnor_b64 %[r2a], %[r2a], %[rsa]\n\t"              \
-  "s_xnor_b64 %[r1a], %[r1a], %[rsa]\n\t"              \
-  "s_xnor_b64 %[r0a], %[r0a], %[rsa]\n\t"              \
-  "s_xnor_b64 %[r2b], %[r2b], %[rsb]\n\t"              \
-  "s_xnor_b64 %[r1b], %[r1b], %[rsb]\n\t"              \
-  "s_xnor_b64 %[r0b], %[r0b], %[rsb]\n\t"              \
-  TQ_PUSH(w, rsa) TQ_PUSH(w, r2a) TQ_PUSH(w, r1a) TQ_PUSH(w, r0a) \
-  TQ_PUSH(w, rsb) TQ_PUSH(w, r2b) TQ_PUSH(w, r1b) TQ_PUSH(w, r0b)
-
-template <int VB, int NH>
-__device__ __forceinline__ void index_pair(float ya, float yb, const float* t, uint32_t& wh, uint32_t& wl) {
-  uint64_t rsa, rsb, r0a, r0b;
-  if constexpr (VB == 2) {
-    static_assert(NH == 4, "2-bit pairs fill one word");
-    asm(TQ_IDX2_BODY(w, w, w, w)
-        : [w] "+v"(wh), [rsa] "=&s"(rsa), [rsb] "=&s"(rsb), [r0a] "=&s"(r0a), [r0b] "=&s"(r0b)
-        : [ya] "v"(ya), [yb] "v"(yb), [t0] "v"(t[0])
-        : "vcc");
-  } else if constexpr (VB == 3) {
-    uint64_t r1a, r1b;
-    float ta, tb;
-#define TQ_IDX3_OPERANDS                                                                                   \
-  [rsa] "=&s"(rsa), [rsb] "=&s"(rsb), [r0a] "=&s"(r0a), [r0b] "=&s"(r0b), [r1a] "=&s"(r1a), [r1b] "=&s"(r1b), \
-      [ta] "=&v"(ta), [tb] "=&v"(tb)                                                                       \
-      : [ya] "v"(ya), [yb] "v"(yb), [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2])                        \
-      : "vcc"
-    if constexpr (NH == 6)
-      asm(TQ_IDX3_BODY(w, w, w, w, w, w) : [w] "+v"(wh), TQ_IDX3_OPERANDS);
-    else if constexpr (NH == 4)
-      asm(TQ_IDX3_BODY(wh, wh, wh, wh, wl, wl) : [wh] "+v"(wh), [wl] "+v"(wl), TQ_IDX3_OPERANDS);
-    else if constexpr (NH == 2)
-      asm(TQ_IDX3_BODY(wh, wh, wl, wl, wl, wl) : [wh] "+v"(wh), [wl] "+v"(wl), TQ_IDX3_OPERANDS);
-    else
-      static_assert(NH == 6, "3-bit pairs split 6, 4 + 2 or 2 + 4");
-#undef TQ_IDX3_OPERANDS
-  } else {
-    static_assert(VB == 4 && NH == 8, "4-bit pairs fill one word");
-    uint64_t r1a, r1b, r2a, r2b;
-    float ta, tb, ua, ub, va, vb;
-    asm(TQ_IDX4_BODY
-        : [w] "+v"(wh), [rsa] "=&s"(rsa), [rsb] "=&s"(rsb), [r0a] "=&s"(r0a), [r0b] "=&s"(r0b), [r1a] "=&s"(r1a),
-          [r1b] "=&s"(r1b), [r2a] "=&s"(r2a), [r2b] "=&s"(r2b), [ta] "=&v"(ta), [tb] "=&v"(tb), [ua] "=&v"(ua),
-          [ub] "=&v"(ub), [va] "=&v"(va), [vb] "=&v"(vb)
-        : [ya] "v"(ya), [yb] "v"(yb), [t0] "v"(t[0]), [t1] "v"(t[1]), [t2] "v"(t[2]), [t3] "v"(t[3]),
-          [t4] "v"(t[4]), [t5] "v"(t[5]), [t6] "v"(t[6])
-        : "vcc");
-  }
-}
-#undef TQ_IDX2_BODY
-#undef TQ_IDX3_BODY
-#undef TQ_IDX4_BODY
-#undef TQ_PUSH
-
 // ------------------------------------------------------------------ keys
 template <int D, int KB>
 __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t blk, uint32_t nblk, uint8_t* tile_lds) {

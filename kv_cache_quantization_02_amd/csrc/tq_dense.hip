@@ -236,29 +236,6 @@ __device__ __forceinline__ void dn_split(const dn_f32x4 (&v)[NC][D / 16], dn_u32
   }
 }
 
-// Magnitude part of the Lloyd-Max index: m = HALF + #{thr_j < a} for the
-// 2^(B-1) - 1 ascending positive thresholds, by a branch-free binary search
-// (one compare per level).
-template <int B>
-__device__ __forceinline__ void dn_search(const float* thr, float ay, uint32_t& m) {
-  constexpr uint32_t HALF = 1u << (B - 1);
-  if constexpr (B == 1) {
-    m = HALF;
-  } else if constexpr (B == 2) {
-    m = HALF + (thr[0] < ay ? 1u : 0u);
-  } else if constexpr (B == 3) {
-    const bool c1 = thr[1] < ay;
-    const bool c2 = (c1 ? thr[2] : thr[0]) < ay;
-    m = (c1 ? HALF + 2u : HALF) + (c2 ? 1u : 0u);
-  } else {
-    const bool c1 = thr[3] < ay;
-    const bool c2 = (c1 ? thr[5] : thr[1]) < ay;
-    const float ta = c1 ? thr[4] : thr[0], tb = c1 ? thr[6] : thr[2];
-    const bool c3 = (c2 ? tb : ta) < ay;
-    m = (c1 ? HALF + 4u : HALF) + (c2 ? 2u : 0u) + (c3 ? 1u : 0u);
-  }
-}
-
 // ------------------------------------------------------------- quantize
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
@@ -369,15 +346,27 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
     auto code_tile = [&](int t) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        if constexpr (!QJL) {
+          // codes e = 3 .. 0 of this tile, pushed highest stream position
+          // first: coordinates 4 (t mod 2) + e of piece t / 2 (#{b < u} is
+          // HALF + m above zero and HALF - 1 - m otherwise, m = #{thr < |y|};
+          // a zero row is set below)
+          uint32_t w = 0u;
+          index_pair<B, 2 * B>(acc[c][t][3], acc[c][t][2], thr[c], w, w);
+          index_pair<B, 2 * B>(acc[c][t][1], acc[c][t][0], thr[c], w, w);
+          if (t & 1)
+            piece[c][t >> 1] |= w << (4 * B);
+          else
+            piece[c][t >> 1] = w;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float y = acc[c][t][e];
-          const float ay = __builtin_fabsf(y);
-          uint32_t m = HALF;
-          float mag = pcen[0];
-          if constexpr (QJL) {
+          for (int e = 0; e < 4; ++e) {
+            const float y = acc[c][t][e];
+            const float ay = __builtin_fabsf(y);
+            uint32_t m = HALF;
+            float mag = pcen[0];
             // a linear scan yields the cell's centroid with one select per
-            // threshold (and fewer live registers than the search's muxes)
+            // threshold (and fewer live registers than a search's muxes)
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
               const bool above = thr[c][j] < ay;
@@ -387,16 +376,12 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
               // the table with the count, through scratch memory)
               asm volatile("" : "+v"(mag));
             }
-          } else {
-            dn_search<B>(thr[c], ay, m);
-          }
-          // #{b < u} = HALF + m for y > 0 and HALF - 1 - m = (HALF + m) ^ (2 HALF - 1)
-          // for y < 0; all ones where the sign bit is set (y = +0 lies on the
-          // middle boundary 0, a tie either way; a zero row is set below)
-          const uint32_t neg = (uint32_t)(__float_as_int(y) >> 31);
-          const uint32_t idx = m ^ (neg & (uint32_t)(2 * HALF - 1));
-          piece[c][t >> 1] |= idx << (B * (4 * (t & 1) + e));
-          if constexpr (QJL) {
+            // #{b < u} = HALF + m for y > 0 and HALF - 1 - m = (HALF + m) ^ (2 HALF - 1)
+            // for y < 0; all ones where the sign bit is set (y = +0 lies on the
+            // middle boundary 0, a tie either way; a zero row is set below)
+            const uint32_t neg = (uint32_t)(__float_as_int(y) >> 31);
+            const uint32_t idx = m ^ (neg & (uint32_t)(2 * HALF - 1));
+            piece[c][t >> 1] |= idx << (B * (4 * (t & 1) + e));
             const float yh = __uint_as_float(__float_as_uint(mag) ^ (neg & 0x80000000u));
             const float rho = __builtin_fmaf(-yh, sc[c], y);
             acc[c][t][e] = rho;
