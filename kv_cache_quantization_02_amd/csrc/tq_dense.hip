@@ -97,17 +97,22 @@ __device__ __forceinline__ uint32_t dn_pack_bf16(float lo, float hi) { return pa
 //   kRows (output only, for the product whose data is the A operand):
 //       out(t, n) = NT n + t, so lane n holds NT consecutive coordinates of
 //       four data rows
+//   kGroups (output only, for the MSE quantizer's one product):
+//       out(t, m) = (D/4) (m/4) + 4 t + m%4, so lane-group g holds the
+//       coordinates (D/4) g + [0, D/4): a contiguous run of the row's
+//       bitstream, stored with whole-dword writes
 // With kInterleaved a lane's result j = 4 t + e is its B operand element
 // j = 8 kc + e of the next product, so products chain without any exchange;
 // the four lane-groups of a row load 64 contiguous bytes per instruction; and
 // a lane's 8 codes of chunk q are one B-byte piece of the row's bitstream.
 // The dequantizer writes its rows through kRows, so that every store
 // instruction covers whole rows.
-enum { kInterleaved = 1, kRows = 2 };
+enum { kInterleaved = 1, kRows = 2, kGroups = 3 };
 
 template <int D, int MAP>
 __device__ __forceinline__ int dn_out_coord(int t, int m) {
   if constexpr (MAP == kInterleaved) return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+  else if constexpr (MAP == kGroups) return (D / 4) * (m >> 2) + 4 * t + (m & 3);
   else return (D / 16) * m + t;
 }
 __device__ __forceinline__ int dn_in_coord(int kc, int gp) { return 32 * kc + 8 * gp; }
@@ -117,6 +122,10 @@ __device__ __forceinline__ void dn_out_slot(int o, int& t, int& m) {
     const int r = o & 31;
     t = 2 * (o >> 5) + ((r & 7) >> 2);
     m = 4 * (r >> 3) + (r & 3);
+  } else if constexpr (MAP == kGroups) {
+    const int r = o % (D / 4);
+    t = r >> 2;
+    m = 4 * (o / (D / 4)) + (r & 3);
   } else {
     t = o % (D / 16);
     m = o / (D / 16);
@@ -236,6 +245,23 @@ __device__ __forceinline__ void dn_split(const dn_f32x4 (&v)[NC][D / 16], dn_u32
   }
 }
 
+// Store a lane's run of RB code bytes (RB = d B / 32, a multiple of 2; the
+// run starts RB g bytes into a row of d B / 8 bytes): whole dwords when RB is
+// a multiple of 4 (the run is then dword-aligned), else 16-bit halves.
+template <int RB, int NW>
+__device__ __forceinline__ void dn_store_run(uint8_t* p, const uint32_t (&w)[NW]) {
+  static_assert(RB % 2 == 0 && (RB + 3) / 4 <= NW, "run size");
+  if constexpr (RB % 4 == 0) {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+    for (int i = 0; i < RB / 4; ++i) q[i] = w[i];
+  } else {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+#pragma unroll
+    for (int i = 0; i < RB / 2; ++i) q[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+  }
+}
+
 // ------------------------------------------------------------- quantize
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
@@ -243,7 +269,9 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
   constexpr int NT = C::NT, NK = C::NK, NC = C::NC;
   constexpr int HALF = 1 << (B - 1), NP = HALF - 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::MAT * (QJL ? 2 : 1)];
-  dn_load_matrix<D, false, kInterleaved>(lds, a.rot);
+  // MSE: codes in contiguous runs (kGroups); QJL: the residual chains into
+  // the projection (kInterleaved)
+  dn_load_matrix<D, false, QJL ? kInterleaved : kGroups>(lds, a.rot);
   if constexpr (QJL) dn_load_matrix<D, false, kInterleaved>(lds + C::MAT, a.proj);
   __syncthreads();
 
@@ -280,10 +308,20 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
         dst[c][kc] = adst[c] ? *reinterpret_cast<const dn_u32x4*>(src + 32 * kc) : dn_u32x4{0u, 0u, 0u, 0u};
     }
   };
-  // an 8-coordinate piece of a zero row: every index is #{b < 0} = HALF - 1
+  // a zero row: every index is #{b < 0} = HALF - 1; an 8-coordinate piece
+  // (QJL) or the words of a lane's run of D/4 coordinates (MSE)
+  constexpr int RB = D * B / 32;  // bytes of a lane's run
   uint32_t zpiece = 0u;
 #pragma unroll
   for (int e = 0; e < 8; ++e) zpiece |= (uint32_t)(HALF - 1) << (B * e);
+  uint32_t zrun[NK];
+#pragma unroll
+  for (int q = 0; q < NK; ++q) zrun[q] = 0u;
+#pragma unroll
+  for (int k = 0; k < D / 4; ++k) {
+    zrun[(B * k) >> 5] |= (uint32_t)(HALF - 1) << ((B * k) & 31);
+    if (((B * k) & 31) + B > 32) zrun[((B * k) >> 5) + 1] |= (uint32_t)(HALF - 1) >> (32 - ((B * k) & 31));
+  }
 
   uint32_t tile = blockIdx.x * 4u + wave;
   if (tile * (uint32_t)C::RW >= a.rows) return;
@@ -328,8 +366,9 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
     }
 
     // y = P x, each output tile coded while the next one's products run (MSE).
-    // piece[c][q]: the 8 B-bit codes of coordinates 32 q + 8 g + [0, 8) of
-    // row 16 c + n, stream bytes B (4 q + g) .. of the row
+    // piece[c][]: MSE, the words of the lane's run, coordinates (D/4) g +
+    // [0, D/4) of row 16 c + n (stream bytes RB g ..); QJL, piece[c][q] holds
+    // the 8 codes of coordinates 32 q + 8 g + [0, 8) (stream bytes B (4 q + g) ..)
     dn_f32x4 acc[NC][NT];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -348,16 +387,22 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
       for (int c = 0; c < NC; ++c) {
         if constexpr (!QJL) {
           // codes e = 3 .. 0 of this tile, pushed highest stream position
-          // first: coordinates 4 (t mod 2) + e of piece t / 2 (#{b < u} is
-          // HALF + m above zero and HALF - 1 - m otherwise, m = #{thr < |y|};
-          // a zero row is set below)
+          // first (#{b < u} is HALF + m above zero and HALF - 1 - m
+          // otherwise, m = #{thr < |y|}; a zero row is set below); they are
+          // run coordinates 4 t + e, at run bits 4 B t ..
+          // The products enter the assembly block through one compiler-visible
+          // add: the compiler inserts the wait states a vector read of an MFMA
+          // result needs, which it does not do for an inline-assembly operand
+          // (+0 also turns -0 into +0; both code as the lower middle cell).
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = acc[c][t][e] + 0.0f;
           uint32_t w = 0u;
-          index_pair<B, 2 * B>(acc[c][t][3], acc[c][t][2], thr[c], w, w);
-          index_pair<B, 2 * B>(acc[c][t][1], acc[c][t][0], thr[c], w, w);
-          if (t & 1)
-            piece[c][t >> 1] |= w << (4 * B);
-          else
-            piece[c][t >> 1] = w;
+          index_pair<B, 2 * B>(y[3], y[2], thr[c], w, w);
+          index_pair<B, 2 * B>(y[1], y[0], thr[c], w, w);
+          const int off = 4 * B * t;
+          piece[c][off >> 5] |= w << (off & 31);
+          if ((off & 31) + 4 * B > 32) piece[c][(off >> 5) + 1] |= w >> (32 - (off & 31));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -427,12 +472,16 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
     for (int c = 0; c < NC; ++c) {
       if (nrm[c] == 0.f) {
 #pragma unroll
-        for (int q = 0; q < NK; ++q) piece[c][q] = zpiece;
+        for (int q = 0; q < NK; ++q) piece[c][q] = QJL ? zpiece : zrun[q];
       }
       if (ac[c]) {
         uint8_t* irow = a.idx + pc[c] * (D * B / 8);
+        if constexpr (QJL) {
 #pragma unroll
-        for (int q = 0; q < NK; ++q) store_lane_bits<B>(irow, 4 * q + g, piece[c][q]);
+          for (int q = 0; q < NK; ++q) store_lane_bits<B>(irow, 4 * q + g, piece[c][q]);
+        } else {
+          dn_store_run<RB>(irow + RB * g, piece[c]);
+        }
         if (g == 0) a.norm[pc[c]] = nrm[c];
       }
       if constexpr (QJL) gam[c] = __builtin_sqrtf(dn_sum_groups(gg[c]));

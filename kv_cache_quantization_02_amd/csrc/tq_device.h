@@ -179,7 +179,10 @@ __device__ __forceinline__ void store_lane_bits(uint8_t* row, int sub, uint64_t 
 // Inline assembly because the compiler turns the plain-C form back into
 // select + shift + or.  Every vector read of a mask written by a vector
 // compare sits at least two instructions after it (the required wait
-// states), and all masks are internal to the block.
+// states), and all masks are internal to the block.  The compiler does not
+// add wait states in front of the block for its operands: ya and yb must not
+// come straight from a matrix-core result (pass them through a vector
+// operation first).
 #define TQ_PUSH(W, M) "v_addc_co_u32 %[" #W "], vcc, %[" #W "], %[" #W "], %[" #M "]\n\t"
 
 #define TQ_IDX1_BODY(W0, W1)                           \
