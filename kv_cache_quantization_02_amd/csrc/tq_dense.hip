@@ -65,12 +65,20 @@ __device__ __forceinline__ const uint32_t* dn_boundaries() {
   else return kDnBnd4;
 }
 
-// NC: 16-row column tiles per wave.  The quantizer takes two (each matrix
-// fragment serves 32 rows).  The dequantizer takes one up to d = 128: fewer
-// live registers and more resident waves measured 8-9% faster there, while at
-// d = 256 the doubled fragment reads from LDS cost more than that.
+// NC: 16-row column tiles per wave.  Two let each matrix fragment serve 32
+// rows, one needs half the registers.  The dequantizer takes one up to
+// d = 128: more resident waves measured 8-9% faster there, while at d = 256
+// the doubled fragment reads from LDS cost more than that.  The MSE quantizer
+// takes two (its coding of one output tile overlaps the next tile's
+// products).  The QJL quantizer takes one, except at d = 128 with 1 or 2
+// bits: at d = 128 one tile takes it from 200-262 VGPRs to 116-159, three
+// resident waves per SIMD instead of one or two, which made 3 and 4 bits
+// 23% and 34% faster but 1 and 2 bits 2-3% slower; at d = 64 one tile was
+// 5-13% faster at every width.
 template <int D>
 constexpr int kDeqNC = D <= 128 ? 1 : 2;
+template <int D, int B, bool QJL>
+constexpr int kQuantNC = (!QJL || (D == 128 && B <= 2)) ? 2 : 1;
 template <int D, int NCV>
 struct DenseCfg {
   static constexpr int NT = D / 16;    // result tiles of 16 coordinates
@@ -265,7 +273,7 @@ __device__ __forceinline__ void dn_store_run(uint8_t* p, const uint32_t (&w)[NW]
 // ------------------------------------------------------------- quantize
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
-  using C = DenseCfg<D, 2>;
+  using C = DenseCfg<D, kQuantNC<D, B, QJL>>;
   constexpr int NT = C::NT, NK = C::NK, NC = C::NC;
   constexpr int HALF = 1 << (B - 1), NP = HALF - 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::MAT * (QJL ? 2 : 1)];
@@ -758,7 +766,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
 // matrices once and then loops over row tiles.
 template <int D, int B, bool QJL, bool DEQ>
 unsigned dense_grid(void (*kernel)(DenseArgs), uint32_t rows) {
-  constexpr int rows_per_wave = DenseCfg<D, DEQ ? kDeqNC<D> : 2>::RW;
+  constexpr int rows_per_wave = DenseCfg<D, DEQ ? kDeqNC<D> : kQuantNC<D, B, QJL>>::RW;
   static int per_cu = 0, cus = 0;  // one pair per kernel
   if (per_cu == 0) {
     int occ = 0, dev = 0, n = 0;
