@@ -103,6 +103,18 @@ def _time_us(fn, reps):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def measure_copy(dev, reps=10):
+    """Plain device-to-device copy of 1 GiB on the same GPU: the read+write envelope
+    the codec kernels are compared with (bytes moved = 2 GiB per copy)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    us = _time_us(lambda: dst.copy_(src), reps)
+    del src, dst
+    moved = 2 * (1 << 30)
+    return {"bytes_moved": moved, "us": us, "GBps": moved / (us * 1e-6) / 1e9}
+
+
 def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     """Timings of the cache append and windowed-fetch entry points, outside the
     timed step: the decode-append workload (64 layers x 32 sequences x 8 kv-heads,
@@ -240,8 +252,8 @@ def measure_wide(tq, synth, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1048576)
     ap.add_argument("--no-next", action="store_true",
@@ -347,6 +359,10 @@ def main():
                 "frac": phases[dom]["GBps"] / HBM_PEAK_GBS, "traffic": measured_traffic(kname),
                 "kernel": phases[dom]["kernel"], "algorithmic_bytes_per_launch": dom_bytes}
 
+    copy = measure_copy(dev)
+    for p in phases.values():
+        p["frac_of_copy"] = p["GBps"] / copy["GBps"]
+
     next_rows = None
     if not args.no_next:
         next_rows = measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev)
@@ -379,6 +395,7 @@ def main():
                    "parallelism": "single GPU"},
         "phases": phases,
         "roofline": roofline,
+        "copy_envelope": copy,
         "cpu_baseline": cpu,
         "next_rows": next_rows,
     }
