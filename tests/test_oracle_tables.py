@@ -92,3 +92,42 @@ def test_frozen_table_shape(bits):
     assert np.all(np.diff(c) > 0) and np.all(np.diff(b) > 0)
     assert np.all(c[:-1] < b) and np.all(b < c[1:])
     assert np.array_equal(c, -c[::-1]) and b[n // 2 - 1] == 0
+
+
+MAX1960 = os.path.join(os.path.dirname(__file__), "golden", "max1960_gaussian_quantizers.txt")
+
+
+def _max_table():
+    out, cur = {}, None
+    for line in open(MAX1960):
+        if not line.strip() or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        if key == "N":
+            cur = out.setdefault(int(vals[0]), {})
+        else:
+            cur[key] = vals
+    return out
+
+
+def _unit(s):
+    # one unit in the last printed decimal place of a table entry
+    return 10.0 ** -(len(s.split(".")[1]) if "." in s else 0)
+
+
+@pytest.mark.parametrize("levels", [4, 8, 16])
+def test_tables_match_max_1960(levels):
+    """The oracle's iteration against the classical published Gaussian quantizers:
+    an external anchor for the 2- and 4-bit tables (and the 3-bit one) that the
+    pages do not print."""
+    row = _max_table()[levels]
+    bits = levels.bit_length() - 1
+    c, b, _ = lloyd_max.lloyd_max_normal(bits)
+    n = len(c)
+    for s, v in zip(row["y"], c[n // 2:]):
+        assert abs(float(s) - v) <= _unit(s) * 1.0001, (levels, "y", s, v)
+    for s, v in zip(row["x"], b[n // 2 - 1:]):
+        assert abs(float(s) - v) <= _unit(s) * 1.0001, (levels, "x", s, v)
+    if "mse" in row:
+        s = row["mse"][0]
+        assert abs(float(s) - lloyd_max.distortion(c, b)) <= _unit(s) * 1.0001
