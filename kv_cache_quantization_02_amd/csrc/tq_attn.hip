@@ -1000,9 +1000,14 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   // The matrix-core kernel streams through per-wave DMA stages, which pay a
   // pipeline fill per block: aim at one round of resident blocks (two per CU
   // on the 256 CUs of gfx950).  The VALU kernel prefers more, shorter blocks.
+  // Each split of the matrix-core kernel also keeps at least four steps per
+  // wave, so that the fill is paid over several steps and the combine does
+  // not merge dozens of tiny splits (one sequence, 4 kv heads, 16384 tokens
+  // at d = 256: 64 splits of 2 steps took 47 us, 32 of 4 take 33 us).
   const long long target = mfma ? 512 : 2048;
+  const long long min_steps = mfma ? 4 : 1;
   long long s = (target + units - 1) / units;
-  const long long max_s = (max_ctx + step - 1) / step;
+  const long long max_s = (max_ctx + min_steps * step - 1) / (min_steps * step);
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   long long tps = (max_ctx + s - 1) / s;

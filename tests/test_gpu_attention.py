@@ -195,7 +195,7 @@ def test_multi_query_matches_decode_at_m1():
     assert torch.equal(a.view(torch.int16), b.reshape(B, Hq, d).view(torch.int16))
 
 
-@pytest.mark.parametrize("Hq,Hkv,N,d,kb,vb,ctx", [(4, 1, 5000, 128, 8, 3, [4999]), (12, 2, 3000, 256, 8, 3, [3000]),
+@pytest.mark.parametrize("Hq,Hkv,N,d,kb,vb,ctx", [(4, 1, 9000, 128, 8, 3, [8999]), (12, 2, 9000, 256, 8, 3, [9000]),
                                                   (8, 2, 2600, 512, 5, 2, [2600])])
 def test_many_splits_block_merge(Hq, Hkv, N, d, kb, vb, ctx):
     # one sequence and few kv heads: the context is cut into 16+ splits, merged
