@@ -138,7 +138,7 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     sch = tq.scheme(d, kb, vb)
 
     def fetch(rot):
-        st = tq.tq_fetch_kv(sch, planes, B, Hkv, Hkv * N, N, lens, N, sig, rot, kw, vw)
+        st = tq.tq_fetch_kv(sch, planes, B, Hkv, Hkv * N, N, N, lens, N, sig, rot, kw, vw)
         assert st == 0, st
     us_e = _time_us(lambda: fetch(False), 10)
     us_r = _time_us(lambda: fetch(True), 10)

@@ -94,7 +94,10 @@ int32_t tq_check_scheme(const tq_scheme* scheme);
  * "Algorithm", bytes paragraph).  Host only, pure. */
 int64_t tq_plane_row_bytes(const tq_scheme* scheme, int32_t plane);
 
-/* Sum of the five planes' row bytes, or a negative TQ_E_* code. */
+/* Sum of the five planes' row bytes, or a negative TQ_E_* code: the bytes
+ * one token-head occupies in the cache, 200 at k8v3 d=128 (TurboQuant page,
+ * "Algorithm", bytes paragraph; TurboQuant KV design page, "Algorithm").
+ * Host only, pure. */
 int64_t tq_row_bytes(const tq_scheme* scheme);
 
 /* Copies the library's value codebook for `bits` in {1,2,3,4,5,8} into host
@@ -156,18 +159,22 @@ int32_t tq_append_kv(const tq_scheme* scheme, const uint16_t* k_bf16, const uint
  * active window; "Deferred inverse FWHT": the V window may stay in the
  * rotated domain so that attention un-rotates its output once).
  *   cache          : planes addressed as in tq_append_kv
- *   lens           : device int32[batch]; tokens t < lens[b] are live
+ *   capacity       : cache tokens per (sequence, kv head); no cache row at or
+ *                    past it is read
+ *   lens           : device int32[batch]; tokens t < min(lens[b], capacity)
+ *                    are live
  *   window         : tokens per output row block (>= every lens[b] the caller
- *                    wants whole); output rows t >= lens[b] are written as +0
+ *                    wants whole, and may exceed the capacity); output rows
+ *                    that are not live are written as +0
  *   values_rotated : 0 -> V as tq_dequantize_kv (signs needed);
  *                    1 -> V rows are centroid[idx] * scale16 rounded to bf16,
  *                    no transform and no signs (signs may be NULL)
  *   k_bf16, v_bf16 : [batch, n_kv_heads, window, head_dim], either may be NULL
  * Keys are always dequantized as in tq_dequantize_kv.  Returns TQ_OK or TQ_E_*. */
 int32_t tq_fetch_kv(const tq_scheme* scheme, const tq_planes* cache, int32_t batch, int32_t n_kv_heads,
-                    int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* lens, int32_t window,
-                    const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16, uint16_t* v_bf16,
-                    void* stream);
+                    int64_t seq_stride_rows, int64_t head_stride_rows, int32_t capacity, const int32_t* lens,
+                    int32_t window, const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16,
+                    uint16_t* v_bf16, void* stream);
 
 /* Un-rotate bf16 rows: out = bf16(signs * FWHT(in) / sqrt(d)), the transform
  * first and the signs last -- the inverse of the value rotation.  This is
@@ -185,7 +192,10 @@ int32_t tq_unrotate_rows(int32_t head_dim, const uint16_t* in_bf16, const tq_row
                          uint16_t* out_bf16, const tq_rows* out_rows, void* stream);
 
 /* Workspace bytes tq_decode_attn_quant needs for these sizes (host only);
- * 0 when the arguments are invalid. */
+ * 0 when the arguments are invalid.  The workspace holds one (m, l,
+ * rotated-domain accumulator) partial per query row and context split; the
+ * combine merges them and applies the inverse rotation once per row
+ * (TurboQuant page, "Deferred inverse FWHT"). */
 size_t tq_decode_attn_workspace_bytes(const tq_scheme* scheme, int32_t batch, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t max_ctx);
 
@@ -203,7 +213,11 @@ size_t tq_decode_attn_workspace_bytes(const tq_scheme* scheme, int32_t batch, in
  *               sequence with 0 tokens gets an all-zero output row
  *   max_ctx   : cache capacity in tokens (>= 1); sizes the launch
  *   out_bf16  : [batch, n_q_heads, head_dim]
- *   workspace : device scratch of >= tq_decode_attn_workspace_bytes() bytes */
+ *   workspace : device scratch of >= tq_decode_attn_workspace_bytes() bytes
+ * Planes may hold any finite scale and zero (fractions and subnormals
+ * included): keys enter as (idx + zero16) * scale16 in float32.  A NaN or
+ * infinite scale or zero in a visible row makes the result unspecified
+ * (the dequantize and fetch calls define those cases bit for bit). */
 int32_t tq_decode_attn_quant(const tq_scheme* scheme, const uint16_t* q_bf16, int32_t batch,
                              int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache,
                              int64_t seq_stride_rows, int64_t head_stride_rows,
@@ -295,7 +309,9 @@ int32_t tq_dense_dequantize(const tq_dense_scheme* scheme, const tq_dense_planes
                             const uint16_t* rot_bf16, const uint16_t* proj_bf16, uint16_t* x_bf16,
                             const tq_rows* out_rows, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (the TQ_E_* codes above; the pages
+ * ask that unsupported head dims be refused up front, TurboQuant page,
+ * "Architecture in mlx-bun").  Host only. */
 const char* tq_status_string(int32_t status);
 
 #ifdef __cplusplus

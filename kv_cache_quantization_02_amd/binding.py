@@ -78,8 +78,9 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
         L.tq_append_kv.restype = ctypes.c_int32
         L.tq_fetch_kv.argtypes = [P(Scheme), P(Planes), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
-                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+                                  ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p]
         L.tq_fetch_kv.restype = ctypes.c_int32
         L.tq_unrotate_rows.argtypes = [ctypes.c_int32, ctypes.c_void_p, P(Rows), ctypes.c_void_p, ctypes.c_void_p,
                                        P(Rows), ctypes.c_void_p]
@@ -174,10 +175,10 @@ def tq_append_kv(scheme, k, v, batch, n_new, n_kv_heads, signs, cache, seq_strid
                               capacity, _stream(stream))
 
 
-def tq_fetch_kv(scheme, cache, batch, n_kv_heads, seq_stride_rows, head_stride_rows, lens, window, signs,
-                values_rotated, k_out, v_out, stream=None) -> int:
+def tq_fetch_kv(scheme, cache, batch, n_kv_heads, seq_stride_rows, head_stride_rows, capacity, lens, window,
+                signs, values_rotated, k_out, v_out, stream=None) -> int:
     return lib().tq_fetch_kv(ctypes.byref(scheme), ctypes.byref(cache), batch, n_kv_heads, seq_stride_rows,
-                             head_stride_rows, _ptr(lens), window, _ptr(signs), int(values_rotated),
+                             head_stride_rows, capacity, _ptr(lens), window, _ptr(signs), int(values_rotated),
                              _ptr(k_out), _ptr(v_out), _stream(stream))
 
 
@@ -314,14 +315,15 @@ def append_kv(k: torch.Tensor, v: torch.Tensor, cache: dict, positions: torch.Te
 
 def fetch_kv(cache: dict, lens: torch.Tensor, window: int, signs: torch.Tensor | None, head_dim: int,
              k_bits: int, v_bits: int, values_rotated: bool = False, keys: bool = True, values: bool = True):
-    """bf16 [B, Hkv, window, d] K and V of a [B, Hkv, capacity, bytes] cache; rows t >= lens[b] are +0.
+    """bf16 [B, Hkv, window, d] K and V of a [B, Hkv, capacity, bytes] cache; rows t >= min(lens[b],
+    capacity) are +0 (the window may be longer than the capacity).
     With values_rotated the V rows stay in the rotated domain (centroid * scale)."""
     B, H, cap = cache["k_q"].shape[:3]
     dev = cache["k_q"].device
     k_out = torch.empty((B, H, window, head_dim), dtype=torch.bfloat16, device=dev) if keys else None
     v_out = torch.empty((B, H, window, head_dim), dtype=torch.bfloat16, device=dev) if values else None
-    _check(tq_fetch_kv(scheme(head_dim, k_bits, v_bits), planes_struct(cache), B, H, H * cap, cap, lens, window,
-                       signs, values_rotated, k_out, v_out), "tq_fetch_kv")
+    _check(tq_fetch_kv(scheme(head_dim, k_bits, v_bits), planes_struct(cache), B, H, H * cap, cap, cap, lens,
+                       window, signs, values_rotated, k_out, v_out), "tq_fetch_kv")
     return k_out, v_out
 
 

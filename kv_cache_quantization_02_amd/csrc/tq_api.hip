@@ -223,9 +223,9 @@ int32_t tq_append_kv(const tq_scheme* s, const uint16_t* k_bf16, const uint16_t*
 }
 
 int32_t tq_fetch_kv(const tq_scheme* s, const tq_planes* cache, int32_t batch, int32_t n_kv_heads,
-                    int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* lens, int32_t window,
-                    const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16, uint16_t* v_bf16,
-                    void* stream) {
+                    int64_t seq_stride_rows, int64_t head_stride_rows, int32_t capacity, const int32_t* lens,
+                    int32_t window, const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16,
+                    uint16_t* v_bf16, void* stream) {
   int32_t st = check_scheme(s);
   if (st != TQ_OK) return st;
   if ((st = check_planes(cache)) != TQ_OK) return st;
@@ -233,7 +233,7 @@ int32_t tq_fetch_kv(const tq_scheme* s, const tq_planes* cache, int32_t batch, i
   if (v_bf16 && !values_rotated && !signs) return TQ_E_NULL;
   if ((k_bf16 && !aligned16(k_bf16)) || (v_bf16 && !aligned16(v_bf16)) || (signs && !aligned16(signs)))
     return TQ_E_ALIGN;
-  if (batch < 0 || n_kv_heads < 0 || window < 0 || seq_stride_rows < 0 || head_stride_rows < 0)
+  if (batch < 0 || n_kv_heads < 0 || window < 0 || capacity < 0 || seq_stride_rows < 0 || head_stride_rows < 0)
     return TQ_E_SHAPE;
   // rows (b, g, t) of the cache window -> a contiguous [batch, n_kv_heads, window, d]
   // output; the token is the fastest index, so a wave's rows are consecutive
@@ -258,6 +258,7 @@ int32_t tq_fetch_kv(const tq_scheme* s, const tq_planes* cache, int32_t batch, i
   a.in = map_of(&in);
   a.out = map_of(&out);
   a.in_len = lens;
+  a.in_cap = capacity;
   a.rotated = values_rotated ? 1 : 0;
   return hip_status(tq::launch_dequantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
                                           kMaxCodecBlocks));
@@ -303,17 +304,25 @@ size_t tq_decode_attn_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t
   return tq_attn_quant_workspace_bytes(s, batch, 1, n_q_heads, n_kv_heads, max_ctx);
 }
 
-int32_t tq_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, int32_t n_queries,
-                      int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache, int64_t seq_stride_rows,
-                      int64_t head_stride_rows, const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
-                      const int8_t* signs, uint16_t* out_bf16, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates an attention call and fills every argument but the partials'
+// buffer (a->part); *need is that buffer's size in bytes.  TQ_OK with
+// a->batch == 0 means there is nothing to launch.
+int32_t attn_prepare(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, int32_t n_queries,
+                     int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache, int64_t seq_stride_rows,
+                     int64_t head_stride_rows, const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
+                     const int8_t* signs, uint16_t* out_bf16, tq::AttnArgs* a, size_t* need) {
   int32_t st = check_scheme(s);
   if (st != TQ_OK) return st;
   if (batch < 0 || n_queries < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1 ||
       seq_stride_rows < 0 || head_stride_rows < 0)
     return TQ_E_SHAPE;
   if ((int64_t)batch * n_queries * n_q_heads >= ((int64_t)1 << 31)) return TQ_E_SHAPE;
+  *a = tq::AttnArgs{};
+  *need = 0;
   if (batch == 0) return TQ_OK;
   if (!q_bf16 || !ctx_lens || !signs || !out_bf16) return TQ_E_NULL;
   if ((st = check_planes(cache)) != TQ_OK) return st;
@@ -321,31 +330,46 @@ int32_t tq_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch,
   int splits = 0, tps = 0;
   tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_queries, n_q_heads, n_kv_heads, max_ctx,
                            &splits, &tps);
-  if (!workspace ||
-      workspace_bytes < tq::decode_attn_part_bytes(s->head_dim, batch, n_queries, n_q_heads, splits))
-    return TQ_E_WORKSPACE;
+  *need = tq::decode_attn_part_bytes(s->head_dim, batch, n_queries, n_q_heads, splits);
+  a->q = q_bf16;
+  a->k_q = (const uint8_t*)cache->k_q;
+  a->k_scale = (const uint16_t*)cache->k_scale;
+  a->k_zero = (const uint16_t*)cache->k_zero;
+  a->v_q = (const uint8_t*)cache->v_q;
+  a->v_scale = (const uint16_t*)cache->v_scale;
+  a->signs = signs;
+  a->ctx_lens = ctx_lens;
+  a->out = out_bf16;
+  a->seq_stride = seq_stride_rows;
+  a->head_stride = head_stride_rows;
+  a->batch = batch;
+  a->n_q_heads = n_q_heads;
+  a->n_kv_heads = n_kv_heads;
+  a->max_ctx = max_ctx;
+  a->splits = splits;
+  a->tokens_per_split = tps;
+  a->softmax_scale = softmax_scale;
+  a->n_queries = n_queries;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tq_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, int32_t n_queries,
+                      int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache, int64_t seq_stride_rows,
+                      int64_t head_stride_rows, const int32_t* ctx_lens, int32_t max_ctx, float softmax_scale,
+                      const int8_t* signs, uint16_t* out_bf16, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  tq::AttnArgs a;
+  size_t need = 0;
+  const int32_t st = attn_prepare(s, q_bf16, batch, n_queries, n_q_heads, n_kv_heads, cache, seq_stride_rows,
+                                  head_stride_rows, ctx_lens, max_ctx, softmax_scale, signs, out_bf16, &a, &need);
+  if (st != TQ_OK || a.batch == 0) return st;
+  if (!workspace || workspace_bytes < need) return TQ_E_WORKSPACE;
   if (!aligned16(workspace)) return TQ_E_ALIGN;
-  tq::AttnArgs a{};
-  a.q = q_bf16;
-  a.k_q = (const uint8_t*)cache->k_q;
-  a.k_scale = (const uint16_t*)cache->k_scale;
-  a.k_zero = (const uint16_t*)cache->k_zero;
-  a.v_q = (const uint8_t*)cache->v_q;
-  a.v_scale = (const uint16_t*)cache->v_scale;
-  a.signs = signs;
-  a.ctx_lens = ctx_lens;
-  a.out = out_bf16;
   a.part = (float*)workspace;
-  a.seq_stride = seq_stride_rows;
-  a.head_stride = head_stride_rows;
-  a.batch = batch;
-  a.n_q_heads = n_q_heads;
-  a.n_kv_heads = n_kv_heads;
-  a.max_ctx = max_ctx;
-  a.splits = splits;
-  a.tokens_per_split = tps;
-  a.softmax_scale = softmax_scale;
-  a.n_queries = n_queries;
   return hip_status(tq::launch_decode_attn(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream));
 }
 

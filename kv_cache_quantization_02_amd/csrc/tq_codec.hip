@@ -563,6 +563,12 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
 // Row offsets travel through LDS too; a negative offset marks a row past the end.
 constexpr int kTileBytes = 64 * 80;  // 64 lanes x (64 + 16 pad) bytes
 
+// Both halves of a bf16 pair with every NaN rewritten as 0x7FC0.
+__device__ __forceinline__ uint32_t canon_bf16x2(uint32_t p) {
+  const uint32_t lo = p & 0xFFFFu, hi = p >> 16;
+  return (((lo & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : lo) | ((((hi & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : hi) << 16);
+}
+
 __device__ __forceinline__ int tile_offset(int chunk) { return 16 * chunk + 16 * (chunk >> 2); }
 
 template <int D>
@@ -620,8 +626,8 @@ __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint3
       split_row(act[u] ? r : 0u, a.split, s, t, h);
       const int64_t irow = row_index(a.in, s, t, h);
       orow[u] = row_index(a.out, s, t, h);
-      // tokens past a fetch window are not read and come out as +0
-      live[u] = act[u] && (!a.in_len || (int64_t)h < (int64_t)a.in_len[s]);
+      // tokens past a fetch window or the cache capacity are not read and come out as +0
+      live[u] = act[u] && (!a.in_len || (int64_t)h < min((int64_t)a.in_len[s], (int64_t)a.in_cap));
 #pragma unroll
       for (int i = 0; i < KW; ++i) wv[u][i] = 0;
       if (live[u]) {
@@ -649,16 +655,26 @@ __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint3
       const float s16 = live[u] ? canon_nan(sc[u]) : 0.f, z16 = live[u] ? canon_nan(zp[u]) : 0.f;
       float k[32];
       if constexpr (KB == 8) {
-        // idx + zero == (idx + 128) + (zero - 128) exactly: both are integers
-        // far below 2^24 (or zero is infinite/NaN, which both forms carry)
-        const float zb = z16 - 128.0f;
+        if (__all(z16 == __builtin_rintf(z16))) {
+          // Every zero point of the wave is an integer (or infinite), as the
+          // quantizer writes them: idx + zero == (idx + 128) + (zero - 128)
+          // exactly, both terms being integers far below 2^24, and the biased
+          // byte converts in one instruction.
+          const float zb = z16 - 128.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t b = wv[u][i] ^ 0x80808080u;
-          k[4 * i] = ((float)(b & 0xFFu) + zb) * s16;
-          k[4 * i + 1] = ((float)((b >> 8) & 0xFFu) + zb) * s16;
-          k[4 * i + 2] = ((float)((b >> 16) & 0xFFu) + zb) * s16;
-          k[4 * i + 3] = ((float)((b >> 24) & 0xFFu) + zb) * s16;
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t b = wv[u][i] ^ 0x80808080u;
+            k[4 * i] = ((float)(b & 0xFFu) + zb) * s16;
+            k[4 * i + 1] = ((float)((b >> 8) & 0xFFu) + zb) * s16;
+            k[4 * i + 2] = ((float)((b >> 16) & 0xFFu) + zb) * s16;
+            k[4 * i + 3] = ((float)((b >> 24) & 0xFFu) + zb) * s16;
+          }
+        } else {
+          // Any other fp16 zero point (a fraction, a subnormal, NaN): the
+          // signed index is converted exactly and added in one rounding.
+#pragma unroll
+          for (int i = 0; i < 32; ++i)
+            k[i] = ((float)(int32_t)(int8_t)(wv[u][i >> 2] >> (8 * (i & 3))) + z16) * s16;
         }
       } else {
 #pragma unroll
@@ -672,6 +688,12 @@ __device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint3
       uint32_t o[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[i] = pack_bf16x2(k[2 * i], k[2 * i + 1]);
+      // finite scale and zero give finite keys; a non-finite one can give a
+      // NaN of any sign or payload (0 * Inf, Inf - Inf), written as 0x7FC0
+      if (__any(!(__builtin_isfinite(s16) && __builtin_isfinite(z16)))) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] = canon_bf16x2(o[i]);
+      }
       store_tile<D>(o, a.k, act[u] ? orow[u] * D : -1, tile, offs, lane, g, rw);
     });
   }
@@ -713,10 +735,7 @@ __device__ __forceinline__ void dequant_value_group(const uint32_t (&wv)[VB], fl
   }
   if constexpr (CANON) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t lo = o[i] & 0xFFFFu, hi = o[i] >> 16;
-      o[i] = (((lo & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : lo) | ((((hi & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : hi) << 16);
-    }
+    for (int i = 0; i < 16; ++i) o[i] = canon_bf16x2(o[i]);
   }
   store_tile<D>(o, base, off, tile, offs, lane, g, rw);
 }
@@ -761,7 +780,7 @@ __device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uin
       split_row(act[u] ? r : 0u, a.split, s, t, h);
       const int64_t irow = row_index(a.in, s, t, h);
       orow[u] = row_index(a.out, s, t, h);
-      live[u] = act[u] && (!a.in_len || (int64_t)h < (int64_t)a.in_len[s]);
+      live[u] = act[u] && (!a.in_len || (int64_t)h < min((int64_t)a.in_len[s], (int64_t)a.in_cap));
       scb[u] = 0.f;
 #pragma unroll
       for (int i = 0; i < VB; ++i) wv[u][i] = 0;
@@ -938,9 +957,7 @@ __global__ __launch_bounds__(256) void unrotate_kernel(UnrotateArgs a) {
     uint32_t o[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t p = pack_bf16x2(w[2 * i] * m, w[2 * i + 1] * m) ^ smask[i];
-      const uint32_t lo = p & 0xFFFFu, hi = p >> 16;
-      o[i] = (((lo & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : lo) | ((((hi & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : hi) << 16);
+      o[i] = canon_bf16x2(pack_bf16x2(w[2 * i] * m, w[2 * i + 1] * m) ^ smask[i]);
     }
     store_tile<D>(o, a.out, act ? orow * D : -1, tile, offs, lane, g, rw);
   }

@@ -58,10 +58,12 @@ struct DequantArgs {
   uint32_t rows;
   RowSplit split;
   RowMap in, out;
-  // Windowed fetch: when in_len is set, rows (s, t, h) with h >= in_len[s]
-  // are not read and are written as +0 (the fetch puts the token index last,
-  // so that consecutive rows are consecutive tokens of one kv head).
+  // Windowed fetch: when in_len is set, rows (s, t, h) with
+  // h >= min(in_len[s], in_cap) are not read and are written as +0 (the fetch
+  // puts the token index last, so that consecutive rows are consecutive
+  // tokens of one kv head).
   const int32_t* in_len;
+  int32_t in_cap;
   // Values left in the rotated domain: centroid * scale16, no transform or signs.
   int32_t rotated;
 };

@@ -151,3 +151,70 @@ def qjl_projection(head_dim: int, seed: int = 44) -> np.ndarray:
     """[d, d] matrix of iid N(0, 1) entries (numpy PCG64, ``seed``) as bf16 patterns."""
     rng = np.random.default_rng(seed)
     return _bf16_of_f64(rng.standard_normal((head_dim, head_dim)))
+
+
+# ------------------------------------------------- arbitrary plane contents
+# Decoders must accept any bytes a plane can hold, not only what the quantizer
+# writes: the TurboQuant page's decoder edge suites cover zero, signed zero,
+# fp16 subnormals and large scales, and a follow-up adds NaNs, infinities and
+# arbitrary zero-point fractions ("Packed-value decode fusion investigation").
+
+# fp16 patterns of those cases: +-0, the smallest and largest subnormals, the
+# smallest normal, +-65504, +-Inf, NaNs of several payloads and signs, 1, -1,
+# a fraction (0x3555 ~ 0.333) and 2^-5.
+FP16_SPECIAL = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x83FF, 0x0400, 0x7BFF, 0xFBFF,
+                         0x7C00, 0xFC00, 0x7E00, 0x7C01, 0xFE00, 0xFFFF, 0x3C00, 0xBC00, 0x3555,
+                         0x1400], dtype=np.uint16)
+FP16_SPECIAL_FINITE = FP16_SPECIAL[(FP16_SPECIAL & 0x7C00) != 0x7C00]
+
+
+def _fp16_any(rng, shape, special):
+    """Half uniformly random 16-bit patterns, a quarter drawn from `special`,
+    a quarter finite with a random fraction and exponent field 1..30."""
+    out = rng.integers(0, 1 << 16, size=shape, dtype=np.uint64).astype(np.uint16)
+    pick = rng.random(shape)
+    sp = pick < 0.25
+    out[sp] = special[rng.integers(0, len(special), size=int(sp.sum()))]
+    fin = (pick >= 0.25) & (pick < 0.5)
+    n = int(fin.sum())
+    out[fin] = ((rng.integers(0, 2, n) << 15) | (rng.integers(1, 31, n) << 10)
+                | rng.integers(0, 1024, n)).astype(np.uint16)
+    return out
+
+
+def arbitrary_planes(lead, row_bytes: dict, seed: int, bounded: bool = False) -> dict:
+    """Random contents for the five planes, shaped lead + [row bytes]
+    (k_q, v_q as uint8; k_scale, k_zero, v_scale as uint16 fp16 patterns).
+
+    Index bytes are uniform.  With bounded=False every fp16 element is
+    arbitrary (any pattern, NaN and infinities included).  With bounded=True
+    they are finite: zero points arbitrary (fractions, subnormals, signed
+    zeros, up to +-65504), each key scale a random fp16 whose magnitude keeps
+    (|zero| + 128) * |scale| below 4, subnormal or zero now and then, so that
+    attention scores stay in a range where softmax is not one-hot; value
+    scales any finite fp16."""
+    rng = np.random.default_rng(seed)
+    lead = tuple(lead)
+    out = {}
+    for n in ("k_q", "v_q"):
+        out[n] = rng.integers(0, 256, size=lead + (row_bytes[n],), dtype=np.uint64).astype(np.uint8)
+    gshape = lead + (row_bytes["k_scale"] // 2,)
+    if not bounded:
+        for n in ("k_scale", "k_zero", "v_scale"):
+            out[n] = _fp16_any(rng, gshape, FP16_SPECIAL)
+        return out
+    zero = _fp16_any(rng, gshape, FP16_SPECIAL_FINITE)
+    bad = (zero & 0x7C00) == 0x7C00
+    zero[bad] &= 0x83FF                      # a non-finite draw becomes a subnormal
+    zmag = np.abs(zero.view(np.float16).astype(np.float64))
+    e = np.ceil(np.log2(zmag + 128.0)).astype(np.int64)      # |zero| + 128 <= 2^e
+    field = 16 - e - rng.integers(0, 7, size=gshape)        # 2^(field - 15) * (1 + f) < 2^(2 - e)
+    field[rng.random(gshape) < 0.1] = 0                     # subnormal or zero scales
+    field = np.clip(field, 0, 30)
+    scale = ((rng.integers(0, 2, size=gshape) << 15) | (field << 10)
+             | rng.integers(0, 1024, size=gshape)).astype(np.uint16)
+    vs = _fp16_any(rng, gshape, FP16_SPECIAL_FINITE)
+    bad = (vs & 0x7C00) == 0x7C00
+    vs[bad] &= 0x83FF
+    out["k_scale"], out["k_zero"], out["v_scale"] = scale, zero, vs
+    return out

@@ -18,6 +18,20 @@ from oracle.tables import codebook
 
 TIE = 1e-6
 
+# Parity record kept for the run's summary: per configuration, the counted
+# boundary-tie index differences (keys, values), the dequantized elements that
+# were not bit-exact, and the rows checked.  tests/conftest.py prints it.
+RECORD: dict = {}
+
+
+def record(config: str, **counts) -> None:
+    r = RECORD.setdefault(config, {})
+    for k, v in counts.items():
+        if isinstance(v, float):
+            r[k] = max(r.get(k, 0.0), v)
+        else:
+            r[k] = r.get(k, 0) + int(v)
+
 
 def _u16(t):
     return np.ascontiguousarray(t).view(np.uint16)

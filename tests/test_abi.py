@@ -146,13 +146,14 @@ def test_append_validation_errors_without_gpu():
 def test_fetch_validation_errors_without_gpu():
     s = tq.scheme(128, 8, 3)
     args = dict(cache=_planes(), batch=4, n_kv_heads=8, seq_stride_rows=8 * 512, head_stride_rows=512,
-                lens=FAKE, window=512, signs=FAKE, values_rotated=0, k_out=FAKE, v_out=FAKE)
+                capacity=512, lens=FAKE, window=512, signs=FAKE, values_rotated=0, k_out=FAKE, v_out=FAKE)
     call = lambda **kw: tq.tq_fetch_kv(s, **{**args, **kw})
     assert call(lens=None) == -3
     assert call(k_out=None, v_out=None) == -3
     assert call(signs=None) == -3                       # eager values need the signs
     assert call(v_out=FAKE + 2) == -5
     assert call(window=-1) == -4
+    assert call(capacity=-1) == -4
     assert call(window=0) == 0          # empty window: no-op
     assert tq.tq_fetch_kv(tq.scheme(100, 8, 3), **args) == -1
 

@@ -1,0 +1,129 @@
+"""GPU decoders on arbitrary plane contents, against the oracle.
+
+The quantizer only ever writes integer zero points and finite or canonical
+planes, so the other GPU tests never show how the decoders treat the rest of
+what a plane can hold.  The TurboQuant page's decoder edge suites cover zero,
+signed zero, fp16 subnormals and large scales, and its nonfinite follow-up
+adds NaNs, infinities and arbitrary zero-point fractions ("Packed-value decode
+fusion investigation").  Here every decoder entry point gets such planes
+(kv_cache_quantization_02_amd.synth.arbitrary_planes; the oracle decodes the
+same bytes):
+
+* tq_dequantize_kv and tq_fetch_kv (eager and rotated values) on arbitrary
+  bytes, NaN and infinities included: bit-exact, every NaN written as 0x7FC0;
+* the fused attention on arbitrary finite planes (fractional, subnormal and
+  signed-zero zero points, large and subnormal scales), at the attention bar.
+  Non-finite planes in attention are outside its contract (tq.h).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_02_amd import binding as tq
+from kv_cache_quantization_02_amd import synth
+from oracle import attention, codec
+from oracle import cache as oc
+from parity import attention_close, record
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SCHEMES = [(d, kb, vb) for d in (64, 128, 256, 512) for kb in (2, 4, 5, 8) for vb in (2, 3, 4, 5, 8)]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _to_gpu(p):
+    return {n: (torch.from_numpy(np.ascontiguousarray(p[n])).to(DEV) if n in ("k_q", "v_q") else
+                torch.from_numpy(np.ascontiguousarray(p[n]).view(np.float16)).to(DEV)) for n in tq.PLANES}
+
+
+def _exact(gpu_bits, ref_bits, what, zero_sign=False):
+    """Bit-exact bf16 outputs; returns (NaN outputs, signed-zero differences).
+    With zero_sign, an exactly-zero output may carry the other sign: the
+    transform's cross-lane stages form the upper element of a pair as the
+    negation of the oracle's difference (the value and un-rotation paths)."""
+    g = np.ascontiguousarray(gpu_bits).view(np.uint16).reshape(-1)
+    r = np.ascontiguousarray(ref_bits).view(np.uint16).reshape(-1)
+    diff = g != r
+    zs = diff & ((g & 0x7FFF) == 0) & ((r & 0x7FFF) == 0)
+    if zero_sign:
+        diff &= ~zs
+    bad = np.nonzero(diff)[0]
+    assert bad.size == 0, (f"{what}: {bad.size} of {g.size} bf16 outputs differ; first at {bad[:4]}: "
+                           f"gpu={[hex(x) for x in g[bad[:4]]]} oracle={[hex(x) for x in r[bad[:4]]]}")
+    nan = (g & 0x7FFF) > 0x7F80
+    assert np.all(g[nan] == 0x7FC0), f"{what}: a NaN output is not 0x7FC0"
+    return int(nan.sum()), int(zs.sum())
+
+
+@pytest.mark.parametrize("d,kb,vb", SCHEMES)
+def test_dequantize_arbitrary_planes(d, kb, vb):
+    L, T, H = 2, 5, 3
+    rb = codec.plane_row_bytes(d, kb, vb)
+    p = synth.arbitrary_planes((L, T, H), rb, seed=d * 100 + kb * 10 + vb)
+    # the smallest subnormal zero point with the largest finite scale, index 0:
+    # k_hat = 2^-24 * 65504, which an integer-only shortcut would lose
+    p["k_q"][0, 0, 0, :4 * kb] = 0          # group 0 of row 0: every index 0
+    p["k_scale"][0, 0, 0, 0] = 0x7BFF
+    p["k_zero"][0, 0, 0, 0] = 0x0001
+    _say(f"[gpu arbitrary] dequantize d={d} k{kb}v{vb}")
+    signs = synth.sign_vector(d)
+    sig = torch.from_numpy(signs).to(DEV)
+    kg, vg = tq.dequantize_kv(_to_gpu(p), sig, d, kb, vb)
+    torch.cuda.synchronize()
+    R = L * T * H
+    flat = {n: p[n].reshape(R, -1) for n in tq.PLANES}
+    kref, vref = codec.dequantize_kv(flat, signs, d, kb, vb)
+    kb16 = synth.bf16_bits(kg).reshape(R, d)
+    nk, _ = _exact(kb16, kref, "keys")
+    nv, zs = _exact(synth.bf16_bits(vg).reshape(R, d), vref, "values", zero_sign=True)
+    assert kref[0, 0] == codec.f32_to_bf16(np.float32(2.0 ** -24) * np.float32(65504.0)) and kb16[0, 0] != 0
+    record("arbitrary planes: dequantize (bit-exact, every scheme)", rows=R, k_nan_outputs=nk, v_nan_outputs=nv,
+           v_zero_sign=zs)
+
+
+@pytest.mark.parametrize("rotated", [False, True])
+@pytest.mark.parametrize("d,kb,vb", [s for s in SCHEMES if s[1] in (8, 4) or s[2] in (3, 5)])
+def test_fetch_arbitrary_planes(d, kb, vb, rotated):
+    B, H, cap = 3, 2, 40
+    lens, window = [40, 17, 0], 48        # the window runs past the capacity: those rows are +0
+    rb = codec.plane_row_bytes(d, kb, vb)
+    c = synth.arbitrary_planes((B, H, cap), rb, seed=7000 + d * 100 + kb * 10 + vb)
+    _say(f"[gpu arbitrary] fetch d={d} k{kb}v{vb} rotated={rotated} lens={lens} window={window} cap={cap}")
+    signs = synth.sign_vector(d)
+    K, V = tq.fetch_kv(_to_gpu(c), torch.tensor(lens, dtype=torch.int32, device=DEV), window,
+                       torch.from_numpy(signs).to(DEV), d, kb, vb, values_rotated=rotated)
+    torch.cuda.synchronize()
+    Kr, Vr = oc.fetch_kv(c, lens, window, signs, d, kb, vb, values_rotated=rotated)
+    _exact(synth.bf16_bits(K), Kr, "fetched keys")
+    _, zs = _exact(synth.bf16_bits(V), Vr, "fetched values", zero_sign=not rotated)
+    assert not synth.bf16_bits(K)[:, :, cap:].any() and not synth.bf16_bits(V)[:, :, cap:].any()
+    record("arbitrary planes: fetch (bit-exact)", rows=B * H * window, v_zero_sign=zs)
+
+
+@pytest.mark.parametrize("d,kb,vb", SCHEMES)
+def test_attention_arbitrary_finite_planes(d, kb, vb):
+    B, Hq, Hkv, N = 2, 8, 2, 300
+    ctx = [300, 77]
+    rb = codec.plane_row_bytes(d, kb, vb)
+    c = synth.arbitrary_planes((B, Hkv, N), rb, seed=9000 + d * 100 + kb * 10 + vb, bounded=True)
+    _say(f"[gpu arbitrary] attention d={d} k{kb}v{vb} B={B} Hq={Hq} Hkv={Hkv} N={N} ctx={ctx}")
+    q = synth.queries(B, Hq, d, 9100 + d)
+    signs = synth.sign_vector(d)
+    out = tq.decode_attn(q.to(DEV), _to_gpu(c), torch.tensor(ctx, dtype=torch.int32, device=DEV),
+                         torch.from_numpy(signs).to(DEV), kb, vb, Hkv)
+    torch.cuda.synchronize()
+    R = B * Hkv * N
+    flat = {n: c[n].reshape(R, -1) for n in tq.PLANES}
+    khat = codec.dequantize_keys_f32(codec.key_indices(flat["k_q"], kb, d), flat["k_scale"], flat["k_zero"])
+    z = codec.dequantize_values_rotated_f32(codec.unpack_bits(flat["v_q"], vb, d).astype(np.int32),
+                                            flat["v_scale"], vb)
+    ref = attention.decode_attention(codec.bf16_to_f32(synth.bf16_bits(q)), khat.reshape(B, Hkv, N, d),
+                                     z.reshape(B, Hkv, N, d), signs, ctx, np.float32(1 / math.sqrt(d)))
+    st = attention_close(synth.bf16_bits(out).reshape(B, Hq, d), ref)
+    _say(f"[gpu arbitrary] attention d={d} k{kb}v{vb}: {st}")
+    record("arbitrary planes: attention (finite)", rows=B * Hq, max_rel_l2=st["max_rel_l2"])

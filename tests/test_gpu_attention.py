@@ -14,7 +14,7 @@ import torch
 from kv_cache_quantization_02_amd import binding as tq
 from kv_cache_quantization_02_amd import synth
 from oracle import attention, codec
-from parity import attention_close
+from parity import attention_close, compare_planes, record
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -102,9 +102,10 @@ def test_misaligned_planes(d, vb):
 
 
 def test_many_steps_ragged_tails():
-    # 1024 (sequence, kv-head) units -> two splits of 512 tokens, four 32-token
-    # steps per wave; the contexts end inside the first step, mid-split and
-    # one token short of the cache
+    # 1024 (sequence, kv-head) units fill the grid without splitting the
+    # context: one split of 1024 tokens per unit, eight 32-token steps per
+    # wave; the contexts end inside the first step, mid-way and one token
+    # short of the cache
     ctx = [1000, 999, 517, 33]
     run_case(4, 256, 256, 1000, 128, 8, 3, ctx, 17, "many steps ragged")
 
@@ -115,7 +116,9 @@ def test_empty_context_gives_zero_rows():
     assert np.all(o[0] == 0)
 
 
-def test_full_size_decode_sampled():
+def test_full_size_decode_pairs():
+    # 32 of the 128 (sequence, kv head) pairs, every query head of each: all kv
+    # heads of the first and last sequence and 16 more drawn at random
     cfg = synth.DECODE_ATTN
     B, Hq, Hkv, d, N = cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"], cfg["context"]
     kb, vb, seed = cfg["k_bits"], cfg["v_bits"], cfg["seed"]
@@ -128,17 +131,35 @@ def test_full_size_decode_sampled():
     ctx_t = torch.full((B,), N, dtype=torch.int32, device=DEV)
     out = tq.decode_attn(q, cache, ctx_t, sig, kb, vb, Hkv)
     torch.cuda.synchronize()
-    for b, g in [(0, 0), (B - 1, Hkv - 1), (7, 3)]:
+    rng = np.random.default_rng(seed)
+    pairs = [(0, g) for g in range(Hkv)] + [(B - 1, g) for g in range(Hkv)]
+    rest = [(b, g) for b in range(1, B - 1) for g in range(Hkv)]
+    pairs += [rest[i] for i in rng.choice(len(rest), size=16, replace=False)]
+    rep = Hq // Hkv
+    worst = {"max_rel_l2": 0.0, "max_abs_err": 0.0}
+    kt = vt = 0
+    for i, (b, g) in enumerate(pairs):
         kr = synth.bf16_bits(k[b, :, g]).reshape(-1, d)
         vr = synth.bf16_bits(v[b, :, g]).reshape(-1, d)
-        khat, z = _oracle_cache(kr, vr, signs, kb, vb, d)
-        rep = Hq // Hkv
+        ref_p = codec.quantize_kv(kr, vr, signs, kb, vb)
+        # the GPU cache rows of this pair against the oracle's planes (ties counted)
+        st_p = compare_planes({n: cache[n][b, g].cpu().numpy() for n in tq.PLANES}, ref_p, d, kb, vb)
+        kt += st_p["key_ties"]
+        vt += st_p["value_ties"]
+        khat = codec.dequantize_keys_f32(ref_p["k_idx"], ref_p["k_scale"], ref_p["k_zero"])
+        z = codec.dequantize_values_rotated_f32(ref_p["v_idx"], ref_p["v_scale"], vb)
         qb = codec.bf16_to_f32(synth.bf16_bits(q[b:b + 1, g * rep:(g + 1) * rep]))
         ref = attention.decode_attention(qb, khat.reshape(1, 1, N, d), z.reshape(1, 1, N, d),
                                          signs, [N], np.float32(1 / math.sqrt(d)))
         got = synth.bf16_bits(out[b:b + 1, g * rep:(g + 1) * rep])
         st = attention_close(got.reshape(1, rep, d), ref)
-        _say(f"[gpu attn] full size (b={b}, kv head {g}): {st}")
+        worst = {key: max(worst[key], st[key]) for key in worst}
+        if i % 8 == 0:
+            _say(f"[gpu attn] full size pair {i + 1}/{len(pairs)} (b={b}, kv head {g}): {st}")
+    record(f"decode attention k8v3 d128 (B{B} Hq{Hq} Hkv{Hkv} ctx{N}, {len(pairs)} of {B * Hkv} pairs)",
+           rows=len(pairs) * N, key_ties=kt, value_ties=vt, max_rel_l2=worst["max_rel_l2"],
+           max_abs_err=worst["max_abs_err"])
+    _say(f"[gpu attn] full size decode: {len(pairs)} pairs, ties k={kt} v={vt}, worst {worst}")
 
 
 def run_mq_case(B, M, Hq, Hkv, N, d, kb, vb, ctx, seed, tag):
@@ -196,11 +217,14 @@ def test_multi_query_matches_decode_at_m1():
 
 
 @pytest.mark.parametrize("Hq,Hkv,N,d,kb,vb,ctx", [(4, 1, 9000, 128, 8, 3, [8999]), (12, 2, 9000, 256, 8, 3, [9000]),
-                                                  (8, 2, 2600, 512, 5, 2, [2600])])
+                                                  (8, 2, 2600, 512, 5, 2, [2600]),
+                                                  (4, 1, 9000, 128, 8, 3, [9000, 700]),
+                                                  (8, 2, 2600, 512, 5, 2, [1, 2600])])
 def test_many_splits_block_merge(Hq, Hkv, N, d, kb, vb, ctx):
-    # one sequence and few kv heads: the context is cut into 16+ splits, merged
-    # by the block-per-row combine
-    B = 1
+    # one or two sequences and few kv heads: the context is cut into 16+
+    # splits, merged by the block-per-row combine; a short second context
+    # leaves most of its splits empty (m = -inf, l = 0) for the merge
+    B = len(ctx)
     sch = tq.scheme(d, kb, vb)
     from kv_cache_quantization_02_amd.binding import lib  # noqa: F401  (library loaded)
     run_case(B, Hq, Hkv, N, d, kb, vb, ctx, 23, f"many splits d{d} k{kb}v{vb}")

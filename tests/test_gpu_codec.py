@@ -11,7 +11,7 @@ import torch
 from kv_cache_quantization_02_amd import binding as tq
 from kv_cache_quantization_02_amd import synth
 from oracle import codec
-from parity import compare_bf16, compare_planes
+from parity import compare_bf16, compare_planes, record
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -38,8 +38,9 @@ def _oracle_planes_to_gpu(ref, lead):
     return out
 
 
-def check_round_trip(k, v, signs, kb, vb, tag):
-    """k, v: bf16 CPU tensors [L, T, H, d]."""
+def check_round_trip(k, v, signs, kb, vb, tag, config=None):
+    """k, v: bf16 CPU tensors [L, T, H, d]; the counts go to the parity record
+    under `config` (default: the tag)."""
     L, T, H, d = k.shape
     R = L * T * H
     _say(f"[gpu codec] {tag}: rows={R} d={d} k{kb}v{vb}")
@@ -62,6 +63,8 @@ def check_round_trip(k, v, signs, kb, vb, tag):
     if stats["value_ties"] == 0:
         compare_bf16(_bits(vg).reshape(R, d), vref, "value round trip")
     _say(f"[gpu codec] {tag}: {stats}")
+    record(config or tag, rows=R, key_ties=stats["key_ties"], value_ties=stats["value_ties"],
+           k_inexact=stats["k_dequant_inexact"], v_inexact=stats["v_dequant_inexact"])
     return stats
 
 
@@ -87,7 +90,8 @@ def test_every_scheme_ragged_rows(d, kb, vb):
 def test_roundtrip_config_with_outlier_channels():
     rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS["roundtrip_k8v3_d128"]
     k, v = synth.kv_inputs(rec, L, T, H, d, seed)
-    check_round_trip(k, v, synth.sign_vector(d), kb, vb, "roundtrip_k8v3_d128")
+    check_round_trip(k, v, synth.sign_vector(d), kb, vb, "roundtrip_k8v3_d128",
+                     config=f"roundtrip k8v3 d128 ({L}x{T}x{H}, every row)")
 
 
 def _edge_rows(d):
@@ -172,37 +176,65 @@ def test_zero_rows_is_a_no_op():
 
 
 # ------------------------------------------------------------ full sizes
-def _sample_rows(R, n, seed):
+# Each workload runs at its full size in the benchmark's launch configuration.
+# Whole layers are checked row by row (every row where the oracle is cheap
+# enough), then the checked rows' planes are replaced by the oracle's and the
+# full-size dequantize is checked on them, ties included.
+FULL_CHECK = {
+    # name: (record key, layers checked whole (None = every layer), random extra rows)
+    "decode_append_k8v3_d128": ("decode append k8v3 d128 (64x32x8)", None, 0),
+    "prefill_k8v3_d128": ("prefill k8v3 d128 (64x8192x8)", (0, 63), 4096),
+    "wide_k4v4_d256": ("wide k4v4 d256 (48x4096x4)", (0, 47), 2048),
+    "wide_k5v2_d512": ("wide k5v2 d512 (48x1024x4)", None, 0),
+}
+
+
+def _checked_rows(L, per_layer, layers, extra, seed):
+    if layers is None:
+        return np.arange(L * per_layer)
+    whole = np.concatenate([np.arange(l * per_layer, (l + 1) * per_layer) for l in layers])
     rng = np.random.default_rng(seed)
-    pick = rng.choice(R, size=min(n, R), replace=False)
-    return np.unique(np.concatenate([pick, np.arange(min(64, R)), np.arange(max(0, R - 64), R)]))
+    return np.unique(np.concatenate([whole, rng.choice(L * per_layer, size=extra, replace=False)]))
 
 
-@pytest.mark.parametrize("name", ["decode_append_k8v3_d128", "prefill_k8v3_d128",
-                                  "wide_k4v4_d256", "wide_k5v2_d512"])
-def test_full_size_workloads_sampled(name):
+@pytest.mark.parametrize("name", list(FULL_CHECK))
+def test_full_size_workloads(name):
     rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS[name]
+    key, layers, extra = FULL_CHECK[name]
     _say(f"[gpu codec] full size {name}: {L}x{T}x{H} rows, d={d}")
     k, v = synth.kv_inputs(rec, L, T, H, d, seed, device=DEV)
     signs = synth.sign_vector(d)
     sig = torch.from_numpy(signs).to(DEV)
     planes = tq.quantize_kv(k, v, sig, kb, vb)
-    kg, vg = tq.dequantize_kv(planes, sig, d, kb, vb)
     torch.cuda.synchronize()
     R = L * T * H
-    rows = _sample_rows(R, 4096, seed)
-    ridx = torch.from_numpy(rows).to(DEV)
-    kk = _bits(k.reshape(R, d)[ridx])
-    vv = _bits(v.reshape(R, d)[ridx])
-    ref = codec.quantize_kv(kk, vv, signs, kb, vb)
-    gp = {n: planes[n].reshape(R, -1)[ridx].cpu().numpy() for n in tq.PLANES}
-    st = compare_planes(gp, ref, d, kb, vb)
-    kref, vref = codec.dequantize_kv_f32(ref, signs, d, kb, vb)
-    ko = _bits(kg.reshape(R, d)[ridx])
-    vo = _bits(vg.reshape(R, d)[ridx])
-    # rows with an index tie reconstruct a different (equally valid) code
-    kt = np.any(codec.key_indices(gp["k_q"], kb, d) != ref["k_idx"], axis=1)
-    vt = np.any(codec.unpack_bits(gp["v_q"], vb, d) != ref["v_idx"], axis=1)
-    compare_bf16(ko[~kt], kref[~kt], "key dequant")
-    compare_bf16(vo[~vt], vref[~vt], "value dequant")
-    _say(f"[gpu codec] {name}: sampled {len(rows)} rows, {st}")
+    rows = _checked_rows(L, T * H, layers, extra, seed)
+    flat = {n: planes[n].view(R, -1) for n in tq.PLANES}
+    chunk = 16384 * 128 // d
+    tot = dict(rows=0, key_ties=0, value_ties=0)
+    refs = []
+    for c0 in range(0, len(rows), chunk):
+        ridx = torch.from_numpy(rows[c0:c0 + chunk]).to(DEV)
+        ref = codec.quantize_kv(_bits(k.view(R, d)[ridx]), _bits(v.view(R, d)[ridx]), signs, kb, vb)
+        st = compare_planes({n: flat[n][ridx].cpu().numpy() for n in tq.PLANES}, ref, d, kb, vb)
+        tot["rows"] += len(ridx)
+        tot["key_ties"] += st["key_ties"]
+        tot["value_ties"] += st["value_ties"]
+        # the oracle's planes go into the checked rows for the dequantize check
+        for n in tq.PLANES:
+            a = np.ascontiguousarray(ref[n])
+            t = torch.from_numpy(a.view(np.uint8) if n in ("k_q", "v_q") else a.view(np.float16)).to(DEV)
+            flat[n].index_copy_(0, ridx, t.view(len(ridx), -1))
+        refs.append((ridx, {n: ref[n] for n in tq.PLANES}))
+        if (c0 // chunk) % 4 == 0:
+            _say(f"[gpu codec] {name}: planes of {tot['rows']} / {len(rows)} rows checked")
+    kg, vg = tq.dequantize_kv(planes, sig, d, kb, vb)
+    torch.cuda.synchronize()
+    kin = vin = 0
+    for ridx, ref in refs:
+        kref, vref = codec.dequantize_kv_f32(ref, signs, d, kb, vb)
+        kin += compare_bf16(_bits(kg.view(R, d)[ridx]), kref, f"{name} key dequant")
+        vin += compare_bf16(_bits(vg.view(R, d)[ridx]), vref, f"{name} value dequant")
+    record(key, rows=tot["rows"], key_ties=tot["key_ties"], value_ties=tot["value_ties"],
+           k_inexact=kin, v_inexact=vin)
+    _say(f"[gpu codec] {name}: {tot}, dequant inexact k={kin} v={vin}")
