@@ -81,11 +81,18 @@ def bf16_ulp(x):
     return 2.0 ** (np.maximum(e, -133) - 7)
 
 
-def compare_bf16(gpu_bits: np.ndarray, ref32: np.ndarray, what: str) -> int:
-    """Returns the number of non-bit-exact elements (asserting the tolerance)."""
+def compare_bf16(gpu_bits: np.ndarray, ref32: np.ndarray, what: str, kinds: dict | None = None) -> int:
+    """Returns the number of elements that are not bit-exact (asserting the
+    tolerance).  With `kinds`, adds to kinds["zero_sign"] the elements that
+    differ only in the sign of an exact zero, and to kinds["value"] the
+    others."""
     g = _u16(gpu_bits).reshape(-1)
     r = codec.f32_to_bf16(np.asarray(ref32, np.float32)).reshape(-1)
     bad = np.nonzero(g != r)[0]
+    if kinds is not None:
+        zs = int(np.sum(((g[bad] & 0x7FFF) == 0) & ((r[bad] & 0x7FFF) == 0)))
+        kinds["zero_sign"] = kinds.get("zero_sign", 0) + zs
+        kinds["value"] = kinds.get("value", 0) + int(bad.size) - zs
     if bad.size:
         gv = codec.bf16_to_f32(g[bad]).astype(np.float64)
         rv = np.asarray(ref32, np.float32).reshape(-1)[bad].astype(np.float64)

@@ -55,8 +55,11 @@ def check_round_trip(k, v, signs, kb, vb, tag, config=None):
     ko, vo = tq.dequantize_kv(op, sig, d, kb, vb)
     torch.cuda.synchronize()
     kref, vref = codec.dequantize_kv_f32(ref, signs, d, kb, vb)
-    stats["k_dequant_inexact"] = compare_bf16(_bits(ko).reshape(R, d), kref, "key dequant")
-    stats["v_dequant_inexact"] = compare_bf16(_bits(vo).reshape(R, d), vref, "value dequant")
+    kk, vk = {}, {}
+    compare_bf16(_bits(ko).reshape(R, d), kref, "key dequant", kk)
+    compare_bf16(_bits(vo).reshape(R, d), vref, "value dequant", vk)
+    stats["k_dequant_inexact"], stats["v_dequant_inexact"] = kk["value"], vk["value"]
+    stats["dequant_zero_sign"] = kk["zero_sign"] + vk["zero_sign"]
     # GPU round trip equals the oracle's where no index tie occurred
     if stats["key_ties"] == 0:
         compare_bf16(_bits(kg).reshape(R, d), kref, "key round trip")
@@ -64,7 +67,8 @@ def check_round_trip(k, v, signs, kb, vb, tag, config=None):
         compare_bf16(_bits(vg).reshape(R, d), vref, "value round trip")
     _say(f"[gpu codec] {tag}: {stats}")
     record(config or tag, rows=R, key_ties=stats["key_ties"], value_ties=stats["value_ties"],
-           k_inexact=stats["k_dequant_inexact"], v_inexact=stats["v_dequant_inexact"])
+           k_inexact=stats["k_dequant_inexact"], v_inexact=stats["v_dequant_inexact"],
+           zero_sign=stats["dequant_zero_sign"])
     return stats
 
 
@@ -230,11 +234,12 @@ def test_full_size_workloads(name):
             _say(f"[gpu codec] {name}: planes of {tot['rows']} / {len(rows)} rows checked")
     kg, vg = tq.dequantize_kv(planes, sig, d, kb, vb)
     torch.cuda.synchronize()
-    kin = vin = 0
+    kk, vk = {"value": 0, "zero_sign": 0}, {"value": 0, "zero_sign": 0}
     for ridx, ref in refs:
         kref, vref = codec.dequantize_kv_f32(ref, signs, d, kb, vb)
-        kin += compare_bf16(_bits(kg.view(R, d)[ridx]), kref, f"{name} key dequant")
-        vin += compare_bf16(_bits(vg.view(R, d)[ridx]), vref, f"{name} value dequant")
+        compare_bf16(_bits(kg.view(R, d)[ridx]), kref, f"{name} key dequant", kk)
+        compare_bf16(_bits(vg.view(R, d)[ridx]), vref, f"{name} value dequant", vk)
+    kin, vin = kk["value"], vk["value"]
     record(key, rows=tot["rows"], key_ties=tot["key_ties"], value_ties=tot["value_ties"],
-           k_inexact=kin, v_inexact=vin)
+           k_inexact=kin, v_inexact=vin, zero_sign=kk["zero_sign"] + vk["zero_sign"])
     _say(f"[gpu codec] {name}: {tot}, dequant inexact k={kin} v={vin}")
