@@ -247,6 +247,26 @@ int32_t tq_attn_quant(const tq_scheme* scheme, const uint16_t* q_bf16, int32_t b
                       const int8_t* signs, uint16_t* out_bf16, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* tq_attn_quant for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, with the split partials kept in the
+ * library's own device scratch instead of a caller workspace.  The scratch
+ * is a static device array of TQ_NOALLOC_SCRATCH_BYTES bytes, one copy per
+ * GPU, held from the library's load to the end of the process; its address is
+ * looked up on the first call made with each device current.  `stream` must
+ * belong to the calling thread's current device.  A problem whose partials
+ * need more than TQ_NOALLOC_SCRATCH_BYTES (tq_attn_quant_workspace_bytes) is
+ * rejected with TQ_E_WORKSPACE before anything is launched.  Calls that
+ * overlap on one GPU (other streams, other host threads) share the scratch
+ * and race; order them.  The call itself allocates nothing.  Returns TQ_OK
+ * or a TQ_E_* code (TQ_E_HIP if the scratch cannot be located). */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t tq_attn_quant_noalloc(const tq_scheme* scheme, const uint16_t* q_bf16, int32_t batch, int32_t n_queries,
+                              int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache,
+                              int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* ctx_lens,
+                              int32_t max_ctx, float softmax_scale, const int8_t* signs, uint16_t* out_bf16,
+                              void* stream);
+
 /* ---------------------------------------------------------------------------
  * Paper variant (TurboQuant KV design pages, "Oracle chain": the paper's own
  * codec -- a dense random rotation from the QR decomposition of a Gaussian

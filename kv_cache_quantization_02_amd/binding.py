@@ -101,6 +101,11 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.tq_attn_quant.restype = ctypes.c_int32
+        L.tq_attn_quant_noalloc.argtypes = [
+            P(Scheme), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(Planes),
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.tq_attn_quant_noalloc.restype = ctypes.c_int32
         L.tq_dense_check_scheme.argtypes = [P(DenseScheme)]
         L.tq_dense_check_scheme.restype = ctypes.c_int32
         L.tq_dense_plane_row_bytes.argtypes = [P(DenseScheme), ctypes.c_int32]
@@ -349,6 +354,17 @@ def tq_attn_quant(scheme, q, batch, n_queries, n_q_heads, n_kv_heads, cache, seq
                                ctypes.byref(cache), seq_stride_rows, head_stride_rows, _ptr(ctx_lens), max_ctx,
                                softmax_scale, _ptr(signs), _ptr(out), _ptr(workspace), workspace_bytes,
                                _stream(stream))
+
+
+# Size of the library's device scratch behind tq_attn_quant_noalloc (include/tq.h).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def tq_attn_quant_noalloc(scheme, q, batch, n_queries, n_q_heads, n_kv_heads, cache, seq_stride_rows,
+                          head_stride_rows, ctx_lens, max_ctx, softmax_scale, signs, out, stream=None) -> int:
+    return lib().tq_attn_quant_noalloc(ctypes.byref(scheme), _ptr(q), batch, n_queries, n_q_heads, n_kv_heads,
+                                       ctypes.byref(cache), seq_stride_rows, head_stride_rows, _ptr(ctx_lens),
+                                       max_ctx, softmax_scale, _ptr(signs), _ptr(out), _stream(stream))
 
 
 def attn_quant(q: torch.Tensor, cache: dict, ctx_lens: torch.Tensor, signs: torch.Tensor, k_bits: int,

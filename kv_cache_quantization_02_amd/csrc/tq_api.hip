@@ -2,6 +2,8 @@
 // row-index set-up and kernel dispatch.  Nothing here allocates.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/tq.h"
 #include "tq_codebooks.h"
 #include "tq_launch.h"
@@ -353,6 +355,32 @@ int32_t attn_prepare(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, 
   return TQ_OK;
 }
 
+// Split partials of tq_attn_quant_noalloc.  Each device holds its own copy
+// of this array from the library's load to the end of the process; host code
+// reaches it only through the address hipGetSymbolAddress returns for the
+// device (the array's name on the host is a stand-in, not a device address).
+constexpr size_t kScratchBytes = TQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on the first call made
+// with that device current and kept.
+int32_t device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TQ_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TQ_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -370,6 +398,25 @@ int32_t tq_attn_quant(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch,
   if (!workspace || workspace_bytes < need) return TQ_E_WORKSPACE;
   if (!aligned16(workspace)) return TQ_E_ALIGN;
   a.part = (float*)workspace;
+  return hip_status(tq::launch_decode_attn(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream));
+}
+
+int32_t tq_attn_quant_noalloc(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, int32_t n_queries,
+                              int32_t n_q_heads, int32_t n_kv_heads, const tq_planes* cache,
+                              int64_t seq_stride_rows, int64_t head_stride_rows, const int32_t* ctx_lens,
+                              int32_t max_ctx, float softmax_scale, const int8_t* signs, uint16_t* out_bf16,
+                              void* stream) {
+  tq::AttnArgs a;
+  size_t need = 0;
+  int32_t st = attn_prepare(s, q_bf16, batch, n_queries, n_q_heads, n_kv_heads, cache, seq_stride_rows,
+                            head_stride_rows, ctx_lens, max_ctx, softmax_scale, signs, out_bf16, &a, &need);
+  if (st != TQ_OK || a.batch == 0) return st;
+  if (need > kScratchBytes) return TQ_E_WORKSPACE;
+  void* part = nullptr;
+  if ((st = device_scratch(&part)) != TQ_OK) return st;
+  // every partial the combine reads is written by the split kernel first,
+  // so the scratch needs no clearing between calls
+  a.part = (float*)part;
   return hip_status(tq::launch_decode_attn(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream));
 }
 

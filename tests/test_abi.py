@@ -143,6 +143,25 @@ def test_append_validation_errors_without_gpu():
     assert call(capacity=0) == 0        # nothing fits: no-op
 
 
+def test_noalloc_attention_validation_without_gpu():
+    # every refusal happens on the host, before the library looks up its scratch
+    s = tq.scheme(128, 8, 3)
+    args = dict(q=FAKE, batch=16, n_queries=1, n_q_heads=32, n_kv_heads=8, cache=_planes(),
+                seq_stride_rows=8 * 32768, head_stride_rows=32768, ctx_lens=FAKE, max_ctx=32768,
+                softmax_scale=0.088, signs=FAKE, out=FAKE)
+    call = lambda **kw: tq.tq_attn_quant_noalloc(s, **{**args, **kw})
+    assert tq.tq_attn_quant_workspace_bytes(s, 16, 1, 32, 8, 32768) <= tq.NOALLOC_SCRATCH_BYTES
+    big = dict(batch=64, n_queries=8, n_q_heads=64)
+    assert tq.tq_attn_quant_workspace_bytes(s, 64, 8, 64, 8, 32768) > tq.NOALLOC_SCRATCH_BYTES
+    assert call(**big) == -6            # beyond the scratch: refused, nothing launched
+    assert call(n_q_heads=30) == -4
+    assert call(n_queries=0) == -4
+    assert call(q=None) == -3
+    assert call(out=FAKE + 2) == -5
+    assert call(batch=0) == 0           # no rows: no-op
+    assert tq.tq_attn_quant_noalloc(tq.scheme(96, 8, 3), **args) == -1
+
+
 def test_fetch_validation_errors_without_gpu():
     s = tq.scheme(128, 8, 3)
     args = dict(cache=_planes(), batch=4, n_kv_heads=8, seq_stride_rows=8 * 512, head_stride_rows=512,
