@@ -81,7 +81,8 @@ def test_dequantize_arbitrary_planes(d, kb, vb):
     kb16 = synth.bf16_bits(kg).reshape(R, d)
     nk, _ = _exact(kb16, kref, "keys")
     nv, zs = _exact(synth.bf16_bits(vg).reshape(R, d), vref, "values", zero_sign=True)
-    assert kref[0, 0] == codec.f32_to_bf16(np.float32(2.0 ** -24) * np.float32(65504.0)) and kb16[0, 0] != 0
+    want00 = codec.f32_to_bf16(np.array([2.0 ** -24], np.float32) * np.float32(65504.0))[0]
+    assert kref[0, 0] == want00 and kb16[0, 0] == want00
     record("arbitrary planes: dequantize (bit-exact, every scheme)", rows=R, k_nan_outputs=nk, v_nan_outputs=nv,
            v_zero_sign=zs)
 
