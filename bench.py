@@ -67,27 +67,60 @@ def measured_traffic(kernel: str):
     return None
 
 
-def cpu_baseline(k, v, signs, rows: int):
-    """The oracle as it stands, on the first `rows` rows of the chunk (one core)."""
-    import numpy as np
-    import torch
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_threads() -> int:
+    """Host cores this process may use, capped at 16 (one GPU's share of the box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(k, v, signs, one_core_rows: int):
+    """The oracle as it stands (numpy, float32 per element, quantize then
+    dequantize) on the prefill chunk's rows: every row on all host cores (one
+    thread per core over 32768-row slices; numpy releases the interpreter lock
+    inside its array loops), and the first `one_core_rows` rows on one core."""
+    from concurrent.futures import ThreadPoolExecutor
 
     from kv_cache_quantization_02_amd import synth
     from oracle import codec
     d = k.shape[-1]
-    kk = k.reshape(-1, d)[:rows]
-    vv = v.reshape(-1, d)[:rows]
-    t0 = time.perf_counter()
+    kk = synth.bf16_bits(k.reshape(-1, d))
+    vv = synth.bf16_bits(v.reshape(-1, d))
+    rows = kk.shape[0]
     step = 32768
-    for i in range(0, rows, step):
-        kb = synth.bf16_bits(kk[i:i + step])
-        vb = synth.bf16_bits(vv[i:i + step])
-        p = codec.quantize_kv(kb, vb, signs, 8, 3)
+
+    def work(i):
+        p = codec.quantize_kv(kk[i:i + step], vv[i:i + step], signs, 8, 3)
         codec.dequantize_kv(p, signs, d, 8, 3)
-    dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "token-heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"quantize + dequantize of the first {rows} token-head rows of the "
-                      f"prefill chunk (k8v3, d128), numpy float32 on one host core, {dt:.1f} s"}
+
+    n = _host_threads()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(work, range(0, rows, step)))
+    dt_all = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(0, one_core_rows, step):
+        work(i)
+    dt_one = time.perf_counter() - t0
+    model = _cpu_model()
+    return {"value": rows / dt_all, "unit": "token-heads/s", "cores": n, "kind": "oracle",
+            "sample": f"quantize + dequantize of all {rows} token-head rows of the prefill chunk (k8v3, d128), "
+                      f"numpy float32, {n} threads on {n} host cores, {dt_all:.1f} s",
+            "cpu_model": model,
+            "one_core": {"value": one_core_rows / dt_one, "unit": "token-heads/s", "cores": 1,
+                         "sample": f"the first {one_core_rows} rows on one core, {dt_one:.1f} s"}}
 
 
 def _time_us(fn, reps):
@@ -98,6 +131,24 @@ def _time_us(fn, reps):
     e0.record()
     for _ in range(reps):
         fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def _time_rotating_us(fns, reps):
+    """Mean microseconds per call of fns[i % len(fns)] over `reps` calls after one
+    untimed pass over all of them (each fn works on its own copy of the data, so
+    rotating through copies larger than the 256 MB last-level cache in total keeps
+    every call reading HBM)."""
+    import torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps * 1e3
@@ -168,8 +219,13 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     ctx6 = torch.full((1,), 16384, dtype=torch.int32, device=dev)
     ws6 = torch.empty(tq.tq_decode_attn_workspace_bytes(s256, 1, 24, 4, 16384), dtype=torch.uint8, device=dev)
     o6 = torch.empty((1, 24, 256), dtype=torch.bfloat16, device=dev)
-    us_6 = _time_us(lambda: tq.decode_attn(q6, c6, ctx6, sig256, 8, 3, 4, out=o6, workspace=ws6), 20)
     b6 = 16384 * 4 * tq.tq_row_bytes(s256)
+    # 40 copies of the 26 MB cache (1 GB): every call reads HBM, not the last-level cache
+    copies6 = [c6] + [{n: t.clone() for n, t in c6.items()} for _ in range(39)]
+    us_6 = _time_rotating_us([lambda c=c: tq.decode_attn(q6, c, ctx6, sig256, 8, 3, 4, out=o6, workspace=ws6)
+                              for c in copies6], 80)
+    us_6_warm = _time_us(lambda: tq.decode_attn(q6, c6, ctx6, sig256, 8, 3, 4, out=o6, workspace=ws6), 20)
+    del copies6
     return {
         "append_kv": {"workload": f"decode append k{akb}v{avb} d{dd}: {L}x{T}x{H} rows, 1 token each, one launch",
                       "us": us_a, "token_heads_per_s": rows / (us_a * 1e-6),
@@ -183,8 +239,10 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
         "attn_multi_query": {"workload": f"{M} causal queries per sequence over the {B}x{Hkv}x{N} k{kb}v{vb} cache, "
                                          f"32 query heads",
                              "us": us_m, "cache_GBps": B * Hkv * N * row_bytes / (us_m * 1e-6) / 1e9},
-        "attn_gqa6_d256": {"workload": "head_dim 256, GQA 6 (24 query / 4 kv heads), one query, 16384 tokens, k8v3",
-                           "us": us_6, "cache_GBps": b6 / (us_6 * 1e-6) / 1e9},
+        "attn_gqa6_d256": {"workload": "head_dim 256, GQA 6 (24 query / 4 kv heads), one query, 16384 tokens, k8v3; "
+                                       "calls rotate over 40 copies of the 26 MB cache (HBM-resident)",
+                           "us": us_6, "cache_GBps": b6 / (us_6 * 1e-6) / 1e9,
+                           "us_same_cache_back_to_back": us_6_warm},
     }
 
 
@@ -224,6 +282,80 @@ def measure_dense(tq, synth, k, v, dev):
     return out
 
 
+def measure_latency(tq, synth, dev):
+    """Launch-bound shapes, outside the timed step: the round-trip workload (one
+    layer x 256 tokens x 8 kv-heads, d128 k8v3) as one quantize + one dequantize;
+    the decode-append step (64 layers x 32 sequences x 8 kv-heads, one token each)
+    quantized as one launch over all 16,384 rows and as 64 per-layer launches of
+    256 rows; the d512 k5v2 codec on one layer (1024 tokens x 4 kv-heads); and a
+    one-sequence decode (32 query / 8 kv heads, d128) at 2048 and 8192 tokens,
+    rotating over cache copies that total over 1 GB."""
+    import torch
+    out = {}
+    # round trip
+    rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS["roundtrip_k8v3_d128"]
+    k, v = synth.kv_inputs(rec, L, T, H, d, seed, device=dev)
+    sig = torch.from_numpy(synth.sign_vector(d)).to(dev)
+    pl = tq.alloc_planes(tq.scheme(d, kb, vb), (L, T, H), dev)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+
+    def rt():
+        tq.quantize_kv(k, v, sig, kb, vb, out=pl)
+        tq.dequantize_kv(pl, sig, d, kb, vb, k_out=ko, v_out=vo)
+    us = _time_us(rt, 200)
+    out["roundtrip_k8v3_d128_latency"] = {"workload": f"{L}x{T}x{H} rows, quantize + dequantize (2 launches)",
+                                          "us": us, "token_heads_per_s": L * T * H / (us * 1e-6)}
+    # decode append step
+    rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS["decode_append_k8v3_d128"]
+    k, v = synth.kv_inputs(rec, L, T, H, d, seed, device=dev)
+    sch = tq.scheme(d, kb, vb)
+    pl = tq.alloc_planes(sch, (L, T, H), dev)
+    us_one = _time_us(lambda: tq.quantize_kv(k, v, sig, kb, vb, out=pl), 200)
+    per_layer = [(k[l:l + 1], v[l:l + 1], {n: t[l:l + 1] for n, t in pl.items()}) for l in range(L)]
+
+    def layers():
+        for kl, vl, pll in per_layer:
+            tq.quantize_kv(kl, vl, sig, kb, vb, out=pll)
+    us_64 = _time_us(layers, 20)
+    rows = L * T * H
+    for tag, u, what in (("one_launch", us_one, "one launch over all rows"),
+                         ("per_layer_launches", us_64, f"{L} per-layer launches of {T * H} rows")):
+        out[f"decode_append_step_{tag}"] = {"workload": f"decode append k{kb}v{vb} d{d}: {L}x{T}x{H} rows, {what}",
+                                            "us": u, "token_heads_per_s": rows / (u * 1e-6)}
+    # d512 k5v2, one layer
+    rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS["wide_k5v2_d512"]
+    k, v = synth.kv_inputs(rec, 1, T, H, d, seed, device=dev)
+    sig5 = torch.from_numpy(synth.sign_vector(d)).to(dev)
+    pl = tq.alloc_planes(tq.scheme(d, kb, vb), (1, T, H), dev)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    us_q = _time_us(lambda: tq.quantize_kv(k, v, sig5, kb, vb, out=pl), 200)
+    us_d = _time_us(lambda: tq.dequantize_kv(pl, sig5, d, kb, vb, k_out=ko, v_out=vo), 200)
+    for name, u in (("quantize", us_q), ("dequantize", us_d)):
+        out[f"{name}_wide_k5v2_d512_one_layer"] = {"workload": f"1x{T}x{H} rows, d={d}, k{kb}v{vb}",
+                                                  "us": u, "token_heads_per_s": T * H / (u * 1e-6)}
+    # one-sequence decode, HBM-resident
+    d, kb, vb = 128, 8, 3
+    sch = tq.scheme(d, kb, vb)
+    for n_ctx in (2048, 8192):
+        kc, vc = synth.kv_inputs("normal", 1, n_ctx, 8, d, 1009, device=dev)
+        c0 = tq.quantize_into_cache(kc, vc, sig, kb, vb)
+        del kc, vc
+        nbytes = 8 * n_ctx * tq.tq_row_bytes(sch)
+        copies = [c0] + [{n: t.clone() for n, t in c0.items()} for _ in range(max(1, (1 << 30) // nbytes) - 1)]
+        q1 = synth.queries(1, 32, d, 1010, device=dev)
+        ctx1 = torch.full((1,), n_ctx, dtype=torch.int32, device=dev)
+        ws1 = torch.empty(tq.tq_decode_attn_workspace_bytes(sch, 1, 32, 8, n_ctx), dtype=torch.uint8, device=dev)
+        o1 = torch.empty((1, 32, d), dtype=torch.bfloat16, device=dev)
+        u = _time_rotating_us([lambda c=c: tq.decode_attn(q1, c, ctx1, sig, kb, vb, 8, out=o1, workspace=ws1)
+                               for c in copies], 2 * len(copies))
+        out[f"decode_one_sequence_ctx{n_ctx}"] = {
+            "workload": f"1 sequence, 32 query / 8 kv heads, d{d} k{kb}v{vb}, {n_ctx} tokens; calls rotate over "
+                        f"{len(copies)} cache copies (HBM-resident)",
+            "us": u, "cache_GBps": nbytes / (u * 1e-6) / 1e9}
+        del copies, c0
+    return out
+
+
 def measure_wide(tq, synth, dev):
     """Timings of the codec at the other widths, outside the timed step: d256
     k4v4 (48 layers x 4096 tokens x 4 kv-heads) and d512 k5v2 (48 x 1024 x 4)."""
@@ -255,7 +387,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1048576)
+    ap.add_argument("--cpu-rows", type=int, default=262144, help="rows of the one-core oracle figure")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the separate timings of the cache append / windowed fetch entry points")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -280,7 +412,11 @@ def main():
     signs = synth.sign_vector(d)
     sig = torch.from_numpy(signs).to(dev)
     sch = tq.scheme(d, kb, vb)
-    planes = tq.alloc_planes(sch, (L, T, H), dev)
+    # two plane buffers: each step quantizes into one and dequantizes the other,
+    # written a step earlier, so dequantize reads planes long evicted from the
+    # 256 MB last-level cache (the step's other traffic is 6.8 GB)
+    planes = [tq.alloc_planes(sch, (L, T, H), dev) for _ in range(2)]
+    tq.quantize_kv(k, v, sig, kb, vb, out=planes[1])
     kout = torch.empty_like(k)
     vout = torch.empty_like(v)
     rows_q = L * T * H
@@ -298,11 +434,15 @@ def main():
     rows_a = B * Hkv * N
     torch.cuda.synchronize()
 
+    n_step = [0]
+
     def step(ev=None):
+        i = n_step[0]
+        n_step[0] += 1
         if ev: ev[0].record()
-        tq.quantize_kv(k, v, sig, kb, vb, out=planes)
+        tq.quantize_kv(k, v, sig, kb, vb, out=planes[i & 1])
         if ev: ev[1].record()
-        tq.dequantize_kv(planes, sig, d, kb, vb, k_out=kout, v_out=vout)
+        tq.dequantize_kv(planes[(i + 1) & 1], sig, d, kb, vb, k_out=kout, v_out=vout)
         if ev: ev[2].record()
         tq.decode_attn(q, cache, ctx, sig, kb, vb, Hkv, out=out, workspace=ws)
         if ev: ev[3].record()
@@ -368,6 +508,7 @@ def main():
         next_rows = measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev)
         next_rows.update(measure_dense(tq, synth, k, v, dev))
         next_rows.update(measure_wide(tq, synth, dev))
+        next_rows.update(measure_latency(tq, synth, dev))
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -379,7 +520,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        _log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        _log(f"cpu baseline: oracle on the whole chunk ({_host_threads()} threads) and {args.cpu_rows} rows "
+             "on one core")
         cpu = cpu_baseline(k, v, signs, args.cpu_rows)
 
     value = rows_q / (ms_per_step * 1e-3)
@@ -387,7 +529,7 @@ def main():
         "metric": "KV token-heads quantized/s and HBM GB/s (% of peak), k8v3 d=128; decode-attn GB/s",
         "value": value, "unit": "token-heads/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 in, fp32 arithmetic, k8v3 planes", "data": "synthetic",
+        "dtype": "fp32 codec arithmetic (bf16 in/out, k8v3 planes); decode: int8 x int8 and fp16 x fp16 MFMA, fp32 accumulation", "data": "synthetic",
         "config": {"workload": "prefill chunk k8v3 d128 (64 layers x 8192 tokens x 8 kv-heads) quantize "
                                "+ full dequantize, then fused GQA decode over a 16x8x32768 k8v3 cache "
                                "with 32 query heads",
