@@ -20,7 +20,10 @@ const uint32_t kCen8[] = {TQ_CENTROIDS_8BIT}, kBnd8[] = {TQ_BOUNDARIES_8BIT};
 // Cap on the blocks of each half (keys / values) of a codec launch: 8192
 // four-wave blocks per half keep every one of the 256 CUs loaded while the
 // hardware balances the remainder dynamically.
-constexpr int kMaxCodecBlocks = 8192;
+#ifndef TQ_MAX_CODEC_BLOCKS
+#define TQ_MAX_CODEC_BLOCKS 8192
+#endif
+constexpr int kMaxCodecBlocks = TQ_MAX_CODEC_BLOCKS;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }

@@ -199,6 +199,17 @@ __device__ __forceinline__ bool rows_contiguous(const RowMap& m, const RowSplit&
          m.seq_stride == (int64_t)sp.div_tok.d * sp.div_head.d;
 }
 
+// One int32 from global memory, waited for inside the same asm block.  The
+// append path reads its sequence positions through this: a plain load there
+// sits in a branch of the row loop, and the compiler then waits for every
+// outstanding memory operation (the next tile's copies included) at the top
+// of every iteration, append or not.
+__device__ __forceinline__ int32_t load_i32_now(const int32_t* p) {
+  int32_t v;
+  asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
 // Output row of input row r for the quantize kernels, or -1 when the row is
 // past the end or falls outside the cache window of an append.
 __device__ __forceinline__ int64_t quant_out_row(const QuantArgs& a, uint32_t r, bool contig_out) {
@@ -208,7 +219,7 @@ __device__ __forceinline__ int64_t quant_out_row(const QuantArgs& a, uint32_t r,
   split_row(r, a.split, s, t, h);
   int64_t o = row_index(a.out, s, t, h);
   if (a.out_pos) {
-    const int64_t p = a.out_pos[s];
+    const int64_t p = load_i32_now(a.out_pos + s);
     if (p + t < 0 || p + t >= a.out_cap) return -1;
     o += p * a.out.tok_stride;
   }
@@ -601,58 +612,97 @@ __device__ __forceinline__ void store_tile(const uint32_t (&o)[16], uint16_t* ba
 // so this keeps enough bytes in flight to cover HBM latency.
 constexpr int kBatch = 4;
 
+// Zero bytes that a dequantize lane reads in place of a row it must not read
+// (past the end, or past a fetch window: such rows are not stored, or are
+// stored as +0).  Every lane then issues the same loads whatever its rows, so
+// the compiler can wait for each row's loads alone; with the loads in per-lane
+// branches, the number of loads issued after a row's is not known, and its
+// first use waits for every outstanding memory operation.  32 bytes cover the
+// largest per-lane read (one group's int8 keys).
+__device__ __attribute__((aligned(16))) uint32_t kZeroRow[8] = {};
+
+// Row indices of one dequantize pass (kBatch rows per lane, `step` apart) and
+// which of them are read: rows past the end are not, nor, in a windowed fetch,
+// tokens at or past min(lens[s], capacity) (they come out as +0).  A fetch's
+// lengths are all loaded before any is used, so one wait covers them.
+template <int D>
+__device__ __forceinline__ void pass_rows(const DequantArgs& a, uint32_t base, uint32_t step, int rw,
+                                          int64_t (&irow)[kBatch], int64_t (&orow)[kBatch], bool (&act)[kBatch],
+                                          bool (&live)[kBatch]) {
+  uint32_t seq[kBatch], tok[kBatch];
+  static_for<kBatch>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const uint32_t r = base + u * step + rw;
+    act[u] = r < a.rows;
+    uint32_t s, t, h;
+    split_row(act[u] ? r : 0u, a.split, s, t, h);
+    irow[u] = row_index(a.in, s, t, h);
+    orow[u] = row_index(a.out, s, t, h);
+    // computed here, before the pass's loads: left to the compiler, this
+    // arithmetic sinks below them, and its 64-bit temporaries then share
+    // registers with loaded values, which makes the first use of any row
+    // wait for the loads of all rows
+    asm volatile("" : "+v"(orow[u]));
+    seq[u] = s;
+    tok[u] = h;
+    live[u] = act[u];
+  });
+  if (a.in_len) {
+    int32_t len[kBatch];
+    static_for<kBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      len[u] = a.in_len[seq[u]];  // rows past the end use sequence 0's (not read)
+    });
+    static_for<kBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      live[u] = act[u] && (int64_t)tok[u] < min((int64_t)len[u], (int64_t)a.in_cap);
+    });
+  }
+}
+
 template <int D, int KB>
-__device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint32_t blk, uint32_t nblk) {
+__device__ __forceinline__ void dequantize_keys_rows(const DequantArgs& a, uint32_t blk, uint32_t nblk,
+                                                     uint8_t* tile, int64_t* offs) {
   using L = GroupLanes<D>;
   constexpr int G = D / kGroup;
   constexpr int KW = KB == 8 ? 8 : KB;  // packed words per lane
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][kTileBytes];
-  __shared__ int64_t row_offs[4][L::RPW];
   const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
-  uint8_t* tile = tiles[threadIdx.x >> 6];
-  int64_t* offs = row_offs[threadIdx.x >> 6];
   const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
   const uint32_t step = nblk * 4u * L::RPW;
   for (uint32_t base = wave * L::RPW; base < a.rows; base += kBatch * step) {
     uint32_t wv[kBatch][KW];
-    float sc[kBatch], zp[kBatch];
-    int64_t orow[kBatch];
+    uint32_t sbits[kBatch], zbits[kBatch];  // raw fp16: converted only when used, so
+                                            // every load of the pass is in flight first
+    int64_t irow[kBatch], orow[kBatch];
     bool act[kBatch], live[kBatch];
+    pass_rows<D>(a, base, step, rw, irow, orow, act, live);
+    const uint8_t* const zrow = reinterpret_cast<const uint8_t*>(kZeroRow);
     static_for<kBatch>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      const uint32_t r = base + u * step + rw;
-      act[u] = r < a.rows;
-      uint32_t s, t, h;
-      split_row(act[u] ? r : 0u, a.split, s, t, h);
-      const int64_t irow = row_index(a.in, s, t, h);
-      orow[u] = row_index(a.out, s, t, h);
-      // tokens past a fetch window or the cache capacity are not read and come out as +0
-      live[u] = act[u] && (!a.in_len || (int64_t)h < min((int64_t)a.in_len[s], (int64_t)a.in_cap));
+      const uint8_t* const q = live[u] ? a.k_q + irow[u] * (D * KB / 8) + 4 * KW * g : zrow;
+      const uint16_t* const sp = live[u] ? a.k_scale + irow[u] * G + g : reinterpret_cast<const uint16_t*>(zrow);
+      const uint16_t* const zp = live[u] ? a.k_zero + irow[u] * G + g : reinterpret_cast<const uint16_t*>(zrow);
+      if constexpr (KB == 8) {
+        const uint2* src = reinterpret_cast<const uint2*>(q);
 #pragma unroll
-      for (int i = 0; i < KW; ++i) wv[u][i] = 0;
-      if (live[u]) {
-        if constexpr (KB == 8) {
-          const uint2* src = reinterpret_cast<const uint2*>(a.k_q + irow * D + kGroup * g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint2 v = src[i];
-            wv[u][2 * i] = v.x;
-            wv[u][2 * i + 1] = v.y;
-          }
-        } else {
-          const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k_q + irow * (D * KB / 8) + 4 * KB * g);
-#pragma unroll
-          for (int i = 0; i < KB; ++i) wv[u][i] = src[i];
+        for (int i = 0; i < 4; ++i) {
+          const uint2 v = src[i];
+          wv[u][2 * i] = v.x;
+          wv[u][2 * i + 1] = v.y;
         }
-        sc[u] = f16_value(a.k_scale[irow * G + g]);
-        zp[u] = f16_value(a.k_zero[irow * G + g]);
+      } else {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(q);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) wv[u][i] = src[i];
       }
+      sbits[u] = *sp;
+      zbits[u] = *zp;
     });
     static_for<kBatch>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      // every lane takes part in the tile exchange; rows past the end compute
-      // on zeros and are not stored
-      const float s16 = live[u] ? canon_nan(sc[u]) : 0.f, z16 = live[u] ? canon_nan(zp[u]) : 0.f;
+      // every lane takes part in the tile exchange; rows that are not read
+      // compute on zeros (+0 bits) and are stored as +0 or not at all
+      const float s16 = canon_nan(f16_value(sbits[u])), z16 = canon_nan(f16_value(zbits[u]));
       float k[32];
       if constexpr (KB == 8) {
         if (__all(z16 == __builtin_rintf(z16))) {
@@ -741,18 +791,15 @@ __device__ __forceinline__ void dequant_value_group(const uint32_t (&wv)[VB], fl
 }
 
 template <int D, int VB>
-__device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uint32_t blk, uint32_t nblk) {
+__device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uint32_t blk, uint32_t nblk,
+                                                       uint8_t* tile, int64_t* offs) {
   using L = GroupLanes<D>;
   constexpr int G = D / kGroup;
   __shared__ float cen_lds[1 << VB];
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][kTileBytes];
-  __shared__ int64_t row_offs[4][L::RPW];
   for (int i = threadIdx.x; i < (1 << VB); i += blockDim.x)
     cen_lds[i] = __uint_as_float(centroids<VB>()[i]);
   __syncthreads();
   const int lane = threadIdx.x & 63, g = L::group(lane), rw = L::row(lane);
-  uint8_t* tile = tiles[threadIdx.x >> 6];
-  int64_t* offs = row_offs[threadIdx.x >> 6];
   const uint32_t wave = blk * 4u + (threadIdx.x >> 6);
   const uint32_t step = nblk * 4u * L::RPW;
   uint32_t smask[16];
@@ -769,34 +816,26 @@ __device__ __forceinline__ void dequantize_values_rows(const DequantArgs& a, uin
   const float rd = inv_sqrt_d<D>();
   for (uint32_t base = wave * L::RPW; base < a.rows; base += kBatch * step) {
     uint32_t wv[kBatch][VB];
-    float scb[kBatch];
-    int64_t orow[kBatch];
+    uint32_t sbits[kBatch];  // raw fp16, converted only when used
+    int64_t irow[kBatch], orow[kBatch];
     bool act[kBatch], live[kBatch];
+    pass_rows<D>(a, base, step, rw, irow, orow, act, live);
+    const uint8_t* const zrow = reinterpret_cast<const uint8_t*>(kZeroRow);
     static_for<kBatch>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      const uint32_t r = base + u * step + rw;
-      act[u] = r < a.rows;
-      uint32_t s, t, h;
-      split_row(act[u] ? r : 0u, a.split, s, t, h);
-      const int64_t irow = row_index(a.in, s, t, h);
-      orow[u] = row_index(a.out, s, t, h);
-      live[u] = act[u] && (!a.in_len || (int64_t)h < min((int64_t)a.in_len[s], (int64_t)a.in_cap));
-      scb[u] = 0.f;
+      const uint32_t* const src = reinterpret_cast<const uint32_t*>(
+          live[u] ? a.v_q + irow[u] * (D * VB / 8) + 4 * VB * g : zrow);
+      const uint16_t* const sp = live[u] ? a.v_scale + irow[u] * G + g : reinterpret_cast<const uint16_t*>(zrow);
 #pragma unroll
-      for (int i = 0; i < VB; ++i) wv[u][i] = 0;
-      if (live[u]) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.v_q + irow * (D * VB / 8) + 4 * VB * g);
-#pragma unroll
-        for (int i = 0; i < VB; ++i) wv[u][i] = src[i];
-        scb[u] = f16_value(a.v_scale[irow * G + g]);
-      }
+      for (int i = 0; i < VB; ++i) wv[u][i] = src[i];
+      sbits[u] = *sp;
     });
     static_for<kBatch>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       // the transform needs every lane of the row: inactive rows compute on
       // zeros and skip the store.  Only a non-finite scale can produce NaN;
       // such rows take the variant that keeps every NaN at 0x7FC0.
-      const float sc = canon_nan(scb[u]);
+      const float sc = canon_nan(f16_value(sbits[u]));
       const bool rot = a.rotated != 0, zero = act[u] && !live[u];
       if (__any(!__builtin_isfinite(sc)))
         dequant_value_group<D, VB, true>(wv[u], sc, cen_lds, smask, rd, lane, g, rw, a.v,
@@ -823,15 +862,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
+  // output staging, one tile per wave, shared by the key and value halves
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][kTileBytes];
+  __shared__ int64_t row_offs[4][GroupLanes<D>::RPW];
+  uint8_t* const tile = tiles[threadIdx.x >> 6];
+  int64_t* const offs = row_offs[threadIdx.x >> 6];
   // with one output skipped every block works on the other
   const bool both = a.k && a.v;
   const uint32_t blk = both ? blockIdx.x >> 1 : blockIdx.x;
   const uint32_t nblk = both ? gridDim.x >> 1 : gridDim.x;
   const bool values = both ? (blockIdx.x & 1) : (a.v != nullptr);
   if (values)
-    dequantize_values_rows<D, VB>(a, blk, nblk);
+    dequantize_values_rows<D, VB>(a, blk, nblk, tile, offs);
   else
-    dequantize_keys_rows<D, KB>(a, blk, nblk);
+    dequantize_keys_rows<D, KB>(a, blk, nblk, tile, offs);
 }
 
 // ------------------------------------------------------------- dispatch
