@@ -338,12 +338,21 @@ struct MfmaCfg {
   static constexpr int G = D / kGroup, GW = G / 2, NSET = (G + 3) / 4, NT = D / 16, CH = 32;
   static constexpr int CPR = D / 16, SW = CPR < 8 ? CPR : 8;  // key chunks per row, swizzle span
   static constexpr int W = D * VB / 32;                      // packed value dwords per row
+  static constexpr int RB = 4 * W;                           // packed value bytes per row
   static constexpr int NK = CH * D / 1024;                   // 16-byte DMAs of key rows
   static constexpr int NV = CH * W / 64;                     // 4-byte DMAs of value rows
   static constexpr int SC_DW = CH * GW, NSP = (SC_DW + 63) / 64;  // per fp16 plane
-  static constexpr int NI = NK + NV + 3 * NSP;               // DMA instructions per step
+  static constexpr int NI_TAIL = NK + NV + 3 * NSP;          // DMA instructions of a partial step
+  // A full step can copy its value rows 16 bytes per lane.  When they leave
+  // half an instruction over and the key scale and zero planes of the step
+  // fill exactly that half (d = 128: 2 x 256 bytes), the last instruction's
+  // upper 32 lanes copy those planes, which follow the value rows in the stage.
+  static constexpr bool WIDE = (CH * RB) % 1024 == 512 && 2 * CH * 2 * G == 512;
+  static constexpr int NVW = (CH * RB + 1023) / 1024;        // 16-byte DMAs of values (+ key planes)
+  static constexpr int NI_FULL = WIDE ? NK + NVW + NSP : NI_TAIL;
+  static constexpr int NI = NI_FULL < NI_TAIL ? NI_FULL : NI_TAIL;  // fewest per step (the waits count these)
   static constexpr int OFF_V = CH * D;
-  static constexpr int OFF_KS = OFF_V + NV * 256;
+  static constexpr int OFF_KS = OFF_V + CH * RB;
   static constexpr int OFF_KZ = OFF_KS + NSP * 256;
   static constexpr int OFF_VS = OFF_KZ + NSP * 256;
   static constexpr int STAGE = OFF_VS + NSP * 256;
@@ -354,11 +363,11 @@ struct MfmaCfg {
   static constexpr int OFF_BUF = OFF_STATS + 4 * 4 * 2 * 4;
   static constexpr int EXTRA = OFF_BUF + 1024;
   // three stages when two blocks still fit a CU, else two
-  static constexpr int S = (4 * 3 * STAGE + EXTRA <= 81920 && 2 * NI <= 63) ? 3 : 2;
+  static constexpr int S = (4 * 3 * STAGE + EXTRA <= 81920 && 2 * NI_TAIL <= 63) ? 3 : 2;
   static constexpr int ACC_BYTES = 4 * NT * 4 * 64 * 4;
   static constexpr int BUF = (4 * S * STAGE > ACC_BYTES) ? 4 * S * STAGE : ACC_BYTES;
   static_assert(G % 2 == 0 && (CH * W) % 64 == 0 && (CH * D) % 1024 == 0, "step layout");
-  static_assert((S - 1) * NI <= 63, "vmcnt range");
+  static_assert((S - 1) * NI_TAIL <= 63, "vmcnt range");
 };
 
 // One DMA instruction: each lane copies `size` bytes from base + voff to LDS
@@ -373,6 +382,10 @@ __device__ __forceinline__ void dma_x4(const void* base, uint32_t voff, uint32_t
 }
 __device__ __forceinline__ void dma_x1(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+// 16 bytes per lane from a per-lane 64-bit address.
+__device__ __forceinline__ void dma_x4_addr(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
@@ -391,7 +404,29 @@ __device__ __forceinline__ void attn_dma(const AttnArgs& a, lds_u8* stage, int64
     if (TAIL) t = min(t, tl - 1);
     dma_x4(kb, (uint32_t)(t * D + 16 * ch), lds_addr(stage + 1024 * j));
   }
-  const uint8_t* vb = a.v_q + r0 * (4 * C::W);
+  if (C::WIDE && !TAIL && a.wide) {
+    // value rows, then (upper lanes of the last copy) the key scale and zero planes
+    const uint8_t* const vb = a.v_q + r0 * C::RB;
+#pragma unroll
+    for (int j = 0; j < C::NVW; ++j) {
+      const int s = 64 * j + lane;
+      const void* src = vb + 16 * s;
+      if (j == C::NVW - 1 && lane >= 32) {
+        const uint16_t* const pl = lane < 48 ? a.k_scale : a.k_zero;
+        src = reinterpret_cast<const uint8_t*>(pl + r0 * C::G) + 16 * (lane & 15);
+      }
+      dma_x4_addr(src, lds_addr(stage + C::OFF_V + 1024 * j));
+    }
+    const uint16_t* const vs = a.v_scale + r0 * C::G;
+#pragma unroll
+    for (int j = 0; j < C::NSP; ++j) {
+      int s = 64 * j + lane;
+      if (s >= C::SC_DW) s = C::SC_DW - 1;
+      dma_x1(vs, (uint32_t)(4 * s), lds_addr(stage + C::OFF_VS + 256 * j));
+    }
+    return;
+  }
+  const uint8_t* vb = a.v_q + r0 * C::RB;
 #pragma unroll
   for (int j = 0; j < C::NV; ++j) {
     const int s = 64 * j + lane;
@@ -628,25 +663,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         if (!full && d / GW >= tl) x[k] = 0u;
         mx = pk_max_u16(mx, x[k] & 0x7FFF7FFFu);
       }
-      mx = xor_max_from<GW>(mx);
-      uint32_t rp[GW];
+      // E_g only grows when a scale of group g has an exponent field of at
+      // least E_g + 15, i.e. |bits| > ((E_g + 15) << 10) - 1: after the first
+      // steps that is rare, so the exact cross-lane maximum is taken only
+      // when some lane sees such a scale
+      uint32_t lim[GW];
 #pragma unroll
-      for (int w = 0; w < GW; ++w) {
-        const uint32_t mw = __builtin_amdgcn_readlane(mx, w);
+      for (int w = 0; w < GW; ++w)
+        lim[w] = (uint32_t)(((E[2 * w] + 15) << 10) - 1) | ((uint32_t)(((E[2 * w + 1] + 15) << 10) - 1) << 16);
+      bool over = false;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int g = 2 * w + hf;
-          const int ex = (int)((mw >> (16 * hf + 10)) & 31u);
-          const int en = (ex > 1 ? ex : 1) - 14;
-          if (en > E[g]) {
-            const float f = ldexpf(1.f, E[g] - en);
-            acc[2 * g] *= f;
-            acc[2 * g + 1] *= f;
-            E[g] = en;
+      for (int k = 0; k < PER; ++k) {
+        const int w = (lane + 64 * k) % GW;
+        uint32_t l = lim[0];
+#pragma unroll
+        for (int i = 1; i < GW; ++i)
+          if (w == i) l = lim[i];
+        over = over || pk_max_u16(x[k] & 0x7FFF7FFFu, l) != l;
+      }
+      if (__any(over)) {
+        mx = xor_max_from<GW>(mx);
+#pragma unroll
+        for (int w = 0; w < GW; ++w) {
+          const uint32_t mw = __builtin_amdgcn_readlane(mx, w);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int g = 2 * w + hf;
+            const int ex = (int)((mw >> (16 * hf + 10)) & 31u);
+            const int en = (ex > 1 ? ex : 1) - 14;
+            if (en > E[g]) {
+              const float f = ldexpf(1.f, E[g] - en);
+              acc[2 * g] *= f;
+              acc[2 * g + 1] *= f;
+              E[g] = en;
+            }
           }
         }
-        rp[w] = f16_pow2_neg(E[2 * w]) | (f16_pow2_neg(E[2 * w + 1]) << 16);
       }
+      uint32_t rp[GW];
+#pragma unroll
+      for (int w = 0; w < GW; ++w) rp[w] = f16_pow2_neg(E[2 * w]) | (f16_pow2_neg(E[2 * w + 1]) << 16);
       lds_u16* const vs16 = (lds_u16*)vs;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
@@ -1043,11 +1099,14 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
                          ((uintptr_t)a.k_zero & 3u) == 0 && ((uintptr_t)a.v_scale & 3u) == 0 &&
                          ((uintptr_t)a.v_q & 3u) == 0;
     if (decode_attn_uses_mfma(D, kb, vb) && aligned) {
+      AttnArgs w = a;
+      w.wide = ((uintptr_t)a.v_q & 15u) == 0 && ((uintptr_t)a.k_scale & 15u) == 0 &&
+               ((uintptr_t)a.k_zero & 15u) == 0 && (a.seq_stride & 1) == 0 && (a.head_stride & 1) == 0;
       switch (vb) {
-        case 2: decode_attn_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(a); break;
-        case 3: decode_attn_mfma_kernel<D, 3><<<grid, 256, 0, st>>>(a); break;
-        case 4: decode_attn_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(a); break;
-        default: decode_attn_mfma_kernel<D, 5><<<grid, 256, 0, st>>>(a); break;
+        case 2: decode_attn_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(w); break;
+        case 3: decode_attn_mfma_kernel<D, 3><<<grid, 256, 0, st>>>(w); break;
+        case 4: decode_attn_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(w); break;
+        default: decode_attn_mfma_kernel<D, 5><<<grid, 256, 0, st>>>(w); break;
       }
       launch_combine<D>(a, st);
       return hipGetLastError();

@@ -85,6 +85,10 @@ struct AttnArgs {
   // Query tokens per sequence: query m of sequence b sits at position
   // ctx_b - n_queries + m and sees the cached tokens t <= that position.
   int32_t n_queries;
+  // Set by the launcher when every 16-byte copy of the matrix-core kernel's
+  // wide layout is 16-byte aligned (value and key scale/zero planes at
+  // 16-byte boundaries, even row strides).
+  int32_t wide;
 };
 
 // Inverse rotation of bf16 rows: out = bf16(signs * FWHT(in) / sqrt(d)).
