@@ -7,7 +7,10 @@ Only the tests use this module.  Sources:
   active window dequantized to bf16;
 * TurboQuant page, "Deferred inverse FWHT": the deferred variant hands back
   the value window still in the rotated domain (rounded to bf16 there), and
-  attention un-rotates its output instead.
+  attention un-rotates its output instead;
+* campaign execution-log page, the KV append dispatch probe: a cache's
+  storage grows in 256-token steps, by allocating zero padding and
+  concatenating the old storage in front of it.
 
 Caches here are dicts of numpy planes shaped [B, H, capacity, row_bytes]
 (uint8 for k_q / v_q, uint16 fp16 patterns for the scale and zero planes),
@@ -20,6 +23,30 @@ import numpy as np
 from . import codec
 
 PLANES = ("k_q", "k_scale", "k_zero", "v_q", "v_scale")
+CAPACITY_STEP = 256
+
+
+def grown_capacity(tokens: int) -> int:
+    """The capacity a cache that must hold `tokens` tokens grows to: the
+    smallest whole number of 256-token steps that covers them (0 for 0)."""
+    if tokens < 0:
+        raise ValueError("negative token count")
+    return -(-tokens // CAPACITY_STEP) * CAPACITY_STEP
+
+
+def grow_kv(cache: dict, new_capacity: int) -> dict:
+    """The cache re-laid at `new_capacity` tokens per (sequence, kv head): the
+    old storage concatenated in front of zero padding.  Rows t below both
+    capacities keep their bytes; rows past the old capacity are zero bytes;
+    with a smaller new capacity the rows past it are dropped (a trim)."""
+    out = {}
+    for name in PLANES:
+        old = np.asarray(cache[name])
+        B, H, cap, w = old.shape
+        keep = min(cap, new_capacity)
+        pad = np.zeros((B, H, new_capacity - keep, w), old.dtype)
+        out[name] = np.concatenate([old[:, :, :keep], pad], axis=2)
+    return out
 
 
 def append_kv(cache: dict, k_new: np.ndarray, v_new: np.ndarray, positions, signs: np.ndarray,

@@ -85,3 +85,74 @@ def test_rotated_window_unrotates_to_the_eager_one():
     assert np.array_equal(codec.unrotate(zf, signs),
                           codec.dequantize_values_f32(vidx, np.ascontiguousarray(c["v_scale"][0]).reshape(H * n, -1),
                                                       signs, vb))
+
+
+def test_grown_capacity_takes_whole_256_token_steps():
+    # the cache grows in 256-token steps (campaign execution-log page, KV
+    # append dispatch probe); the depths are the ones that probe ran
+    assert oc.grown_capacity(0) == 0
+    for t, want in [(1, 256), (65, 256), (255, 256), (256, 256), (257, 512), (2048, 2048), (2049, 2304),
+                     (8192, 8192), (8193, 8448)]:
+        assert oc.grown_capacity(t) == want
+    for t in range(0, 2000, 7):
+        c = oc.grown_capacity(t)
+        assert c % 256 == 0 and t <= c < t + 256
+
+
+def test_grow_keeps_rows_and_zero_pads():
+    B, H, cap, d, kb, vb = 3, 2, 7, 64, 4, 3
+    before = _empty(B, H, cap, d, kb, vb, fill=1)
+    after = oc.grow_kv(before, 11)
+    for name in oc.PLANES:
+        assert after[name].shape[:3] == (B, H, 11) and after[name].dtype == before[name].dtype
+        assert np.array_equal(after[name][:, :, :cap], before[name])
+        assert not after[name][:, :, cap:].any()
+    signs = synth.sign_vector(d)
+    lens = [7, 4, 0]
+    for rotated in (False, True):
+        K0, V0 = oc.fetch_kv(before, lens, 9, signs, d, kb, vb, values_rotated=rotated)
+        K1, V1 = oc.fetch_kv(after, lens, 9, signs, d, kb, vb, values_rotated=rotated)
+        assert np.array_equal(K0, K1) and np.array_equal(V0, V1)
+
+
+def test_trim_drops_rows_past_the_new_capacity():
+    B, H, cap, d, kb, vb = 2, 3, 9, 64, 8, 2
+    before = _empty(B, H, cap, d, kb, vb, fill=1)
+    trimmed = oc.grow_kv(before, 5)
+    regrown = oc.grow_kv(trimmed, 9)
+    for name in oc.PLANES:
+        assert np.array_equal(trimmed[name], before[name][:, :, :5])
+        assert np.array_equal(regrown[name][:, :, :5], before[name][:, :, :5])
+        assert not regrown[name][:, :, 5:].any()
+
+
+def test_appends_across_a_growth_boundary_match_one_large_cache():
+    # a stream of tokens appended in chunks into a small cache that grows when
+    # the next chunk would not fit gives the same planes, byte for byte, as
+    # the whole stream appended into a cache created at the final capacity
+    # (both start as zero bytes); B != H so that a transposed (b, g) shows
+    B, H, d, kb, vb = 2, 3, 64, 5, 4
+    chunks = [3, 4, 1, 6, 2]
+    total = sum(chunks)
+    k, v = synth.kv_inputs("normal", B, total, H, d, 24)
+    kb16, vb16 = synth.bf16_bits(k), synth.bf16_bits(v)
+    signs = synth.sign_vector(d)
+    step = 5                                   # a small growth step keeps the oracle fast
+    small = _empty(B, H, step, d, kb, vb)
+    pos = 0
+    grows = 0
+    for n in chunks:
+        cap = small["k_q"].shape[2]
+        if pos + n > cap:
+            small = oc.grow_kv(small, -(-(pos + n) // step) * step)
+            grows += 1
+        small = oc.append_kv(small, kb16[:, pos:pos + n], vb16[:, pos:pos + n], [pos] * B, signs, kb, vb)
+        pos += n
+    assert grows >= 2
+    cap = small["k_q"].shape[2]
+    big = oc.append_kv(_empty(B, H, cap, d, kb, vb), kb16, vb16, [0] * B, signs, kb, vb)
+    for name in oc.PLANES:
+        assert np.array_equal(small[name], big[name])
+    K, V = oc.fetch_kv(small, [total, total - 3], cap, signs, d, kb, vb)
+    Kb, Vb = oc.fetch_kv(big, [total, total - 3], cap, signs, d, kb, vb)
+    assert np.array_equal(K, Kb) and np.array_equal(V, Vb)
