@@ -202,6 +202,18 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
         assert st == 0, st
     us_u = _time_us(unrot, 10)
     del kw, vw, acache
+    # growth of the decode cache by one 256-token step: every kept row read once,
+    # the new storage written once
+    Ng = tq.tq_grown_capacity(N + 1)
+    gcache = tq.alloc_planes(sch, (B, Hkv, Ng), dev)
+    gdst = tq.planes_struct(gcache)
+
+    def grow():
+        st = tq.tq_grow_kv(sch, B, Hkv, planes, Hkv * N, N, N, gdst, Hkv * Ng, Ng, Ng)
+        assert st == 0, st
+    us_g = _time_us(grow, 10)
+    gb = B * Hkv * (N + Ng) * row_bytes
+    del gcache
     # multi-query (speculative, 4 query tokens per sequence) over the same cache
     M = 4
     qm = synth.queries(B * M, 32, d, 1006 + 11, device=dev).reshape(B, M, 32, d)
@@ -234,6 +246,9 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
                            "us": us_e, "GBps": fb / (us_e * 1e-6) / 1e9},
         "fetch_kv_rotated": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache, values rotated",
                              "us": us_r, "GBps": fb / (us_r * 1e-6) / 1e9},
+        "grow_kv": {"workload": f"the {B}x{Hkv}x{N} k{kb}v{vb} cache re-laid at capacity {Ng} "
+                                f"(one 256-token growth step)",
+                    "us": us_g, "GBps": gb / (us_g * 1e-6) / 1e9, "algorithmic_bytes": gb},
         "unrotate_rows": {"workload": f"{B * Hkv * N} bf16 rows of d={d} (the rotated V window)",
                           "us": us_u, "GBps": B * Hkv * N * 4 * d / (us_u * 1e-6) / 1e9},
         "attn_multi_query": {"workload": f"{M} causal queries per sequence over the {B}x{Hkv}x{N} k{kb}v{vb} cache, "

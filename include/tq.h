@@ -52,6 +52,7 @@ extern "C" {
 #define TQ_E_WORKSPACE (-6) /* decode workspace missing or too small             */
 #define TQ_E_HIP (-7)       /* the HIP runtime reported a launch error           */
 #define TQ_E_PLANE (-8)     /* plane index out of range                          */
+#define TQ_E_OVERLAP (-9)   /* an output buffer overlaps an input or itself      */
 
 /* Quantization scheme, validated on every call.  The pages' served sets:
  * head_dim in {64,128,256,512}; k_bits in {2,4,5,8}; v_bits in {2,3,4,5,8}
@@ -175,6 +176,44 @@ int32_t tq_fetch_kv(const tq_scheme* scheme, const tq_planes* cache, int32_t bat
                     int64_t seq_stride_rows, int64_t head_stride_rows, int32_t capacity, const int32_t* lens,
                     int32_t window, const int8_t* signs, int32_t values_rotated, uint16_t* k_bf16,
                     uint16_t* v_bf16, void* stream);
+
+/* Cache capacity grows in steps of this many tokens (campaign execution-log
+ * page, the KV append dispatch probe: growth happens at 256-step
+ * boundaries). */
+#define TQ_CAPACITY_STEP 256
+
+/* The capacity a cache that must hold `tokens` tokens grows to: the smallest
+ * multiple of TQ_CAPACITY_STEP that is >= tokens (0 for 0).  Returns
+ * TQ_E_SHAPE for a negative count or a result past INT32_MAX.  Host only. */
+int64_t tq_grown_capacity(int64_t tokens);
+
+/* Re-lay a [batch, kv-head, capacity] cache at another capacity (campaign
+ * execution-log page, the KV append dispatch probe: a cache that grows
+ * allocates zero padding and concatenates its old storage in front of it).
+ * For every sequence b < batch, kv head g < n_kv_heads and plane:
+ *   dst row t = src row t          t < min(src_capacity, dst_capacity)
+ *   dst row t = zero bytes         min(...) <= t < dst_capacity
+ * so dst_capacity > src_capacity grows the cache and a smaller one trims it
+ * (rows past dst_capacity are dropped).  Source rows past the kept ones are
+ * not read.
+ *   src, dst       : planes; row(b, g, t) = b*seq_stride_rows + g*head_stride_rows + t
+ *                    with each side's own strides (rows of its own planes)
+ *   dst strides    : each (b, g) segment of dst_capacity rows must sit apart:
+ *                    over the axes of extent > 1, the smaller stride s1 (axis
+ *                    extent n1) is >= dst_capacity and the larger is
+ *                    >= (n1 - 1) * s1 + dst_capacity.  [batch, kv-head,
+ *                    capacity] and [kv-head, batch, capacity], padded or not,
+ *                    qualify.
+ * No byte any dst plane writes may lie in a src plane's read range or in
+ * another dst plane (TQ_E_OVERLAP): the call copies, it does not move rows
+ * in place.  A plane whose bases and segment offsets are all 16-byte aligned
+ * (any capacity that is a multiple of 16 at the usual strides) is copied
+ * 16 bytes per lane, otherwise 2 bytes per lane.  Returns TQ_OK or a TQ_E_*
+ * code. */
+int32_t tq_grow_kv(const tq_scheme* scheme, int32_t batch, int32_t n_kv_heads, const tq_planes* src,
+                   int64_t src_seq_stride_rows, int64_t src_head_stride_rows, int32_t src_capacity,
+                   const tq_planes* dst, int64_t dst_seq_stride_rows, int64_t dst_head_stride_rows,
+                   int32_t dst_capacity, void* stream);
 
 /* Un-rotate bf16 rows: out = bf16(signs * FWHT(in) / sqrt(d)), the transform
  * first and the signs last -- the inverse of the value rotation.  This is

@@ -82,6 +82,12 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p]
         L.tq_fetch_kv.restype = ctypes.c_int32
+        L.tq_grown_capacity.argtypes = [ctypes.c_int64]
+        L.tq_grown_capacity.restype = ctypes.c_int64
+        L.tq_grow_kv.argtypes = [P(Scheme), ctypes.c_int32, ctypes.c_int32, P(Planes), ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int32, P(Planes), ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int32, ctypes.c_void_p]
+        L.tq_grow_kv.restype = ctypes.c_int32
         L.tq_unrotate_rows.argtypes = [ctypes.c_int32, ctypes.c_void_p, P(Rows), ctypes.c_void_p, ctypes.c_void_p,
                                        P(Rows), ctypes.c_void_p]
         L.tq_unrotate_rows.restype = ctypes.c_int32
@@ -185,6 +191,17 @@ def tq_fetch_kv(scheme, cache, batch, n_kv_heads, seq_stride_rows, head_stride_r
     return lib().tq_fetch_kv(ctypes.byref(scheme), ctypes.byref(cache), batch, n_kv_heads, seq_stride_rows,
                              head_stride_rows, capacity, _ptr(lens), window, _ptr(signs), int(values_rotated),
                              _ptr(k_out), _ptr(v_out), _stream(stream))
+
+
+def tq_grown_capacity(tokens: int) -> int:
+    return lib().tq_grown_capacity(tokens)
+
+
+def tq_grow_kv(scheme, batch, n_kv_heads, src, src_seq_stride_rows, src_head_stride_rows, src_capacity, dst,
+               dst_seq_stride_rows, dst_head_stride_rows, dst_capacity, stream=None) -> int:
+    return lib().tq_grow_kv(ctypes.byref(scheme), batch, n_kv_heads, ctypes.byref(src), src_seq_stride_rows,
+                            src_head_stride_rows, src_capacity, ctypes.byref(dst), dst_seq_stride_rows,
+                            dst_head_stride_rows, dst_capacity, _stream(stream))
 
 
 def tq_unrotate_rows(head_dim, x, in_rows, signs, out, out_rows, stream=None) -> int:
@@ -316,6 +333,17 @@ def append_kv(k: torch.Tensor, v: torch.Tensor, cache: dict, positions: torch.Te
     _check(tq_append_kv(scheme(d, k_bits, v_bits), k, v, B, n_new, H, signs, planes_struct(cache), H * cap, cap,
                         positions, cap), "tq_append_kv")
     return cache
+
+
+def grow_kv(cache: dict, new_capacity: int, head_dim: int, k_bits: int, v_bits: int) -> dict:
+    """A new [B, Hkv, new_capacity, bytes] cache holding the old rows below both
+    capacities and zero bytes after them (new planes; the old ones are kept)."""
+    B, H, cap = cache["k_q"].shape[:3]
+    sch = scheme(head_dim, k_bits, v_bits)
+    out = alloc_planes(sch, (B, H, new_capacity), cache["k_q"].device)
+    _check(tq_grow_kv(sch, B, H, planes_struct(cache), H * cap, cap, cap, planes_struct(out),
+                      H * new_capacity, new_capacity, new_capacity), "tq_grow_kv")
+    return out
 
 
 def fetch_kv(cache: dict, lens: torch.Tensor, window: int, signs: torch.Tensor | None, head_dim: int,

@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["tq_api.hip", "tq_codec.hip", "tq_attn.hip", "tq_dense.hip"]
+SOURCES = ["tq_api.hip", "tq_codec.hip", "tq_attn.hip", "tq_dense.hip", "tq_cache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -25,6 +25,12 @@ const uint32_t kCen8[] = {TQ_CENTROIDS_8BIT}, kBnd8[] = {TQ_BOUNDARIES_8BIT};
 #endif
 constexpr int kMaxCodecBlocks = TQ_MAX_CODEC_BLOCKS;
 
+// Cap on the blocks of a cache re-lay; a grid-stride loop covers the rest.
+#ifndef TQ_MAX_GROW_BLOCKS
+#define TQ_MAX_GROW_BLOCKS 8192
+#endif
+constexpr int kMaxGrowBlocks = TQ_MAX_GROW_BLOCKS;
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -267,6 +273,108 @@ int32_t tq_fetch_kv(const tq_scheme* s, const tq_planes* cache, int32_t batch, i
   a.rotated = values_rotated ? 1 : 0;
   return hip_status(tq::launch_dequantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
                                           kMaxCodecBlocks));
+}
+
+int64_t tq_grown_capacity(int64_t tokens) {
+  if (tokens < 0) return TQ_E_SHAPE;
+  if (tokens > (int64_t)INT32_MAX - (TQ_CAPACITY_STEP - 1)) return TQ_E_SHAPE;
+  return (tokens + TQ_CAPACITY_STEP - 1) / TQ_CAPACITY_STEP * TQ_CAPACITY_STEP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The (b, g) segments of `cap` consecutive rows at b*ss + g*hs are nested:
+// along the axis of smaller stride they sit one after another, and the
+// other axis steps past that whole run.
+bool segments_apart(int64_t B, int64_t H, int64_t ss, int64_t hs, int64_t cap) {
+  if (cap == 0 || B == 0 || H == 0) return true;
+  if (B == 1 && H == 1) return true;
+  if (B == 1) return hs >= cap;
+  if (H == 1) return ss >= cap;
+  int64_t n1 = H, s1 = hs, s2 = ss;
+  if (ss < hs) {
+    n1 = B;
+    s1 = ss;
+    s2 = hs;
+  }
+  if (s1 < cap) return false;
+  const __int128 run = (__int128)(n1 - 1) * s1 + cap;
+  return (__int128)s2 >= run;
+}
+
+// Byte range [lo, hi) of one plane over B x H segments of `rows` rows.
+struct Span {
+  uintptr_t lo, hi;
+};
+
+bool plane_span(const void* base, int64_t rb, int64_t B, int64_t H, int64_t ss, int64_t hs, int64_t rows,
+                Span* out) {
+  const __int128 last = (__int128)(B - 1) * ss + (__int128)(H - 1) * hs + rows;
+  const __int128 bytes = last * rb;
+  if (bytes > ((__int128)1 << 62)) return false;
+  out->lo = (uintptr_t)base;
+  out->hi = (uintptr_t)base + (uintptr_t)bytes;
+  return true;
+}
+
+bool spans_meet(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t tq_grow_kv(const tq_scheme* s, int32_t batch, int32_t n_kv_heads, const tq_planes* src,
+                   int64_t src_seq_stride_rows, int64_t src_head_stride_rows, int32_t src_capacity,
+                   const tq_planes* dst, int64_t dst_seq_stride_rows, int64_t dst_head_stride_rows,
+                   int32_t dst_capacity, void* stream) {
+  int32_t st = check_scheme(s);
+  if (st != TQ_OK) return st;
+  if (!src || !dst) return TQ_E_NULL;
+  if ((st = check_planes(src)) != TQ_OK) return st;
+  if ((st = check_planes(dst)) != TQ_OK) return st;
+  if (batch < 0 || n_kv_heads < 0 || src_capacity < 0 || dst_capacity < 0 || src_seq_stride_rows < 0 ||
+      src_head_stride_rows < 0 || dst_seq_stride_rows < 0 || dst_head_stride_rows < 0)
+    return TQ_E_SHAPE;
+  if (!segments_apart(batch, n_kv_heads, dst_seq_stride_rows, dst_head_stride_rows, dst_capacity))
+    return TQ_E_SHAPE;
+  if (batch == 0 || n_kv_heads == 0 || dst_capacity == 0) return TQ_OK;
+  const int64_t keep = src_capacity < dst_capacity ? src_capacity : dst_capacity;
+  const void* sp[5] = {src->k_q, src->k_scale, src->k_zero, src->v_q, src->v_scale};
+  void* dp[5] = {dst->k_q, dst->k_scale, dst->k_zero, dst->v_q, dst->v_scale};
+  Span rd[5], wr[5];
+  tq::GrowArgs a{};
+  uint64_t total = 0;
+  for (int p = 0; p < 5; ++p) {
+    const int64_t rb = tq_plane_row_bytes(s, p);
+    if (!plane_span(sp[p], rb, batch, n_kv_heads, src_seq_stride_rows, src_head_stride_rows, keep, &rd[p]) ||
+        !plane_span(dp[p], rb, batch, n_kv_heads, dst_seq_stride_rows, dst_head_stride_rows, dst_capacity,
+                    &wr[p]))
+      return TQ_E_SHAPE;
+    tq::GrowPlane& g = a.plane[p];
+    g.src = (const uint8_t*)sp[p];
+    g.dst = (uint8_t*)dp[p];
+    g.src_seq = src_seq_stride_rows * rb;
+    g.src_head = src_head_stride_rows * rb;
+    g.dst_seq = dst_seq_stride_rows * rb;
+    g.dst_head = dst_head_stride_rows * rb;
+    g.copy = keep * rb;
+    g.dst_bytes = (int64_t)dst_capacity * rb;
+    const uint64_t chunks = (uint64_t)((g.dst_bytes + tq::kGrowChunkBytes - 1) / tq::kGrowChunkBytes);
+    g.chunks = (uint32_t)chunks;
+    g.vec16 = aligned16(sp[p]) && aligned16(dp[p]) && g.src_seq % 16 == 0 && g.src_head % 16 == 0 &&
+              g.dst_seq % 16 == 0 && g.dst_head % 16 == 0;
+    a.first[p] = (uint32_t)total;
+    total += (uint64_t)batch * (uint64_t)n_kv_heads * chunks;
+    if (total > UINT32_MAX) return TQ_E_SHAPE;
+  }
+  for (int p = 0; p < 5; ++p)
+    for (int q = 0; q < 5; ++q)
+      if (spans_meet(wr[p], rd[q]) || (q != p && spans_meet(wr[p], wr[q]))) return TQ_E_OVERLAP;
+  a.total = (uint32_t)total;
+  a.n_kv_heads = (uint32_t)n_kv_heads;
+  return hip_status(tq::launch_grow(a, (hipStream_t)stream, kMaxGrowBlocks));
 }
 
 int32_t tq_unrotate_rows(int32_t head_dim, const uint16_t* in_bf16, const tq_rows* in_rows, const int8_t* signs,
@@ -523,6 +631,7 @@ const char* tq_status_string(int32_t status) {
     case TQ_E_WORKSPACE: return "decode workspace missing or too small";
     case TQ_E_HIP: return "HIP launch error";
     case TQ_E_PLANE: return "plane index out of range";
+    case TQ_E_OVERLAP: return "an output buffer overlaps an input or another output";
     default: return "unknown status";
   }
 }

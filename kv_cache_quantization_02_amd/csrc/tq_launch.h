@@ -118,10 +118,33 @@ struct DenseArgs {
   RowMap x_map, plane_map;
 };
 
+// Re-laying a cache at another capacity.  Each plane is a set of
+// segments, one per (sequence, kv head), of consecutive rows: the first
+// `copy` bytes of a destination segment come from the source segment, the
+// rest up to `dst_bytes` are zero.  Offsets are in bytes.
+struct GrowPlane {
+  const uint8_t* src;
+  uint8_t* dst;
+  int64_t src_seq, src_head, dst_seq, dst_head;
+  int64_t copy, dst_bytes;
+  uint32_t chunks;  // blocks per segment
+  uint32_t vec16;   // every segment start 16-byte aligned on both sides
+};
+
+struct GrowArgs {
+  GrowPlane plane[5];
+  uint32_t first[5];  // first block of each plane; plane p owns [first[p], first[p+1])
+  uint32_t total;     // blocks over all planes
+  uint32_t n_kv_heads;
+};
+
 hipError_t launch_quantize(const QuantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
 hipError_t launch_unrotate(const UnrotateArgs& a, int d, hipStream_t st, int max_blocks);
 hipError_t launch_dequantize(const DequantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks);
 hipError_t launch_decode_attn(const AttnArgs& a, int d, int kb, int vb, hipStream_t st);
+hipError_t launch_grow(const GrowArgs& a, hipStream_t st, int max_blocks);
+// Bytes of one destination segment that one block covers.
+constexpr int64_t kGrowChunkBytes = 256 * 16 * 4;
 
 hipError_t launch_dense_quantize(const DenseArgs& a, int d, int bits, bool qjl, hipStream_t st);
 hipError_t launch_dense_dequantize(const DenseArgs& a, int d, int bits, bool qjl, hipStream_t st);

@@ -234,3 +234,41 @@ def test_dense_validation_errors_without_gpu():
     z = tq.Rows(0, 4, 2, 8, 2, 1)
     assert tq.tq_dense_quantize(s, FAKE, z, FAKE, FAKE, good, z) == 0
     assert tq.tq_dense_dequantize(s, good, z, FAKE, FAKE, FAKE, z) == 0
+
+
+def test_grown_capacity_steps():
+    assert [tq.tq_grown_capacity(t) for t in (0, 1, 255, 256, 257, 2049, 8193)] == \
+        [0, 256, 256, 256, 512, 2304, 8448]
+    assert tq.tq_grown_capacity(2**31 - 256) == 2**31 - 256
+    assert tq.tq_grown_capacity(2**31 - 255) == -4        # past the int32 capacity range
+    assert tq.tq_grown_capacity(-1) == -4
+
+
+def _spread_planes(base):
+    # five plane bases 1 GiB apart, so that only a deliberate overlap meets
+    return tq.Planes(*[base + (i << 30) for i in range(5)])
+
+
+def test_grow_validation_errors_without_gpu():
+    s = tq.scheme(128, 8, 3)
+    src, dst = _spread_planes(1 << 36), _spread_planes(1 << 40)
+    args = dict(batch=4, n_kv_heads=8, src=src, src_seq_stride_rows=8 * 512, src_head_stride_rows=512,
+                src_capacity=512, dst=dst, dst_seq_stride_rows=8 * 768, dst_head_stride_rows=768,
+                dst_capacity=768)
+    call = lambda **kw: tq.tq_grow_kv(s, **{**args, **kw})
+    assert tq.tq_grow_kv(tq.scheme(128, 8, 7), **args) == -2
+    assert call(src=tq.Planes(FAKE, 0, FAKE, FAKE, FAKE)) == -3
+    assert call(dst=tq.Planes(FAKE, FAKE, FAKE, FAKE + 4, FAKE)) == -5
+    assert call(dst_capacity=-1) == -4
+    assert call(src_head_stride_rows=-1) == -4
+    # destination segments that would share rows
+    assert call(dst_head_stride_rows=700) == -4
+    assert call(dst_seq_stride_rows=8 * 768 - 1) == -4
+    assert call(n_kv_heads=1, dst_seq_stride_rows=767) == -4
+    # a destination plane in a source plane's read range, or in another destination plane
+    assert call(dst=tq.Planes((1 << 36) + 4096, *[(1 << 40) + (i << 30) for i in range(1, 5)])) == -9
+    assert call(dst=tq.Planes(1 << 40, (1 << 40) + 1024, *[(1 << 40) + (i << 30) for i in range(2, 5)])) == -9
+    # no rows to write: no-op after validation
+    assert call(batch=0) == 0
+    assert call(dst_capacity=0) == 0
+    assert tq.status_string(-9).startswith("an output buffer overlaps")
