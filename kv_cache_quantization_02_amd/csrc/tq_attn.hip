@@ -459,6 +459,87 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Value scales of one step, in the stage: rows past the context are zeroed;
+// E_g (the least power of two above every scale of group g the wave has
+// seen) is raised where a scale needs it, rescaling the group's accumulators
+// exactly; the scales are rewritten in place as fp16 pairs of consecutive
+// contraction slots (dword (slot / 2) * G + g holds slots 2k, 2k + 1 of
+// group g), multiplied by 2^-E_g, so that the PV A operand reads them as they
+// are.  slot_of(t) is token t's contraction slot.
+template <int D, int VB, typename SlotOf>
+__device__ __forceinline__ void stage_value_scales(lds_u8* sp, bool full, int tl, int lane, int (&E)[D / kGroup],
+                                                   tq_float4 (&acc)[D / 16], SlotOf slot_of) {
+  using C = MfmaCfg<D, VB>;
+  constexpr int G = C::G, GW = C::GW;
+  lds_u32* const vs = (lds_u32*)(sp + C::OFF_VS);
+  constexpr int PER = (C::SC_DW + 63) / 64;
+  uint32_t x[PER], mx = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int d = lane + 64 * k;
+    x[k] = d < C::SC_DW ? vs[d] : 0u;
+    if (!full && d / GW >= tl) x[k] = 0u;
+    mx = pk_max_u16(mx, x[k] & 0x7FFF7FFFu);
+  }
+  // E_g only grows when a scale of group g has an exponent field of at
+  // least E_g + 15, i.e. |bits| > ((E_g + 15) << 10) - 1: after the first
+  // steps that is rare, so the exact cross-lane maximum is taken only
+  // when some lane sees such a scale
+  uint32_t lim[GW];
+#pragma unroll
+  for (int w = 0; w < GW; ++w)
+    lim[w] = (uint32_t)(((E[2 * w] + 15) << 10) - 1) | ((uint32_t)(((E[2 * w + 1] + 15) << 10) - 1) << 16);
+  bool over = false;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int w = (lane + 64 * k) % GW;
+    uint32_t l = lim[0];
+#pragma unroll
+    for (int i = 1; i < GW; ++i)
+      if (w == i) l = lim[i];
+    over = over || pk_max_u16(x[k] & 0x7FFF7FFFu, l) != l;
+  }
+  if (__any(over)) {
+    mx = xor_max_from<GW>(mx);
+#pragma unroll
+    for (int w = 0; w < GW; ++w) {
+      const uint32_t mw = __builtin_amdgcn_readlane(mx, w);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int g = 2 * w + hf;
+        const int ex = (int)((mw >> (16 * hf + 10)) & 31u);
+        const int en = (ex > 1 ? ex : 1) - 14;
+        if (en > E[g]) {
+          const float f = ldexpf(1.f, E[g] - en);
+          acc[2 * g] *= f;
+          acc[2 * g + 1] *= f;
+          E[g] = en;
+        }
+      }
+    }
+  }
+  uint32_t rp[GW];
+#pragma unroll
+  for (int w = 0; w < GW; ++w) rp[w] = f16_pow2_neg(E[2 * w]) | (f16_pow2_neg(E[2 * w + 1]) << 16);
+  lds_u16* const vs16 = (lds_u16*)vs;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int d = lane + 64 * k;
+    const int t = d / GW, w = d % GW;
+    uint32_t rpl = rp[0];
+#pragma unroll
+    for (int i = 1; i < GW; ++i)
+      if (w == i) rpl = rp[i];
+    const uint32_t y = pk_mul_f16(x[k], rpl);
+    const int u = slot_of(t);
+    const int o = 2 * ((u >> 1) * G + 2 * w) + (u & 1);
+    if (d < C::SC_DW) {
+      vs16[o] = (uint16_t)y;
+      vs16[o + 2] = (uint16_t)(y >> 16);
+    }
+  }
+}
+
 template <int D, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_attn_mfma_kernel(AttnArgs a) {
   using C = MfmaCfg<D, VB>;
@@ -652,75 +733,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // ---- value scales: zero rows past the context, track E_g, normalise,
     // and rewrite them in place as fp16 pairs (slot 2k, slot 2k+1) per group,
     // slot 8 (t mod 4) + t / 4 for token t: the A operand of PV reads them as is
-    {
-      lds_u32* const vs = (lds_u32*)(sp + C::OFF_VS);
-      constexpr int PER = (C::SC_DW + 63) / 64;
-      uint32_t x[PER], mx = 0;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int d = lane + 64 * k;
-        x[k] = d < C::SC_DW ? vs[d] : 0u;
-        if (!full && d / GW >= tl) x[k] = 0u;
-        mx = pk_max_u16(mx, x[k] & 0x7FFF7FFFu);
-      }
-      // E_g only grows when a scale of group g has an exponent field of at
-      // least E_g + 15, i.e. |bits| > ((E_g + 15) << 10) - 1: after the first
-      // steps that is rare, so the exact cross-lane maximum is taken only
-      // when some lane sees such a scale
-      uint32_t lim[GW];
-#pragma unroll
-      for (int w = 0; w < GW; ++w)
-        lim[w] = (uint32_t)(((E[2 * w] + 15) << 10) - 1) | ((uint32_t)(((E[2 * w + 1] + 15) << 10) - 1) << 16);
-      bool over = false;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int w = (lane + 64 * k) % GW;
-        uint32_t l = lim[0];
-#pragma unroll
-        for (int i = 1; i < GW; ++i)
-          if (w == i) l = lim[i];
-        over = over || pk_max_u16(x[k] & 0x7FFF7FFFu, l) != l;
-      }
-      if (__any(over)) {
-        mx = xor_max_from<GW>(mx);
-#pragma unroll
-        for (int w = 0; w < GW; ++w) {
-          const uint32_t mw = __builtin_amdgcn_readlane(mx, w);
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int g = 2 * w + hf;
-            const int ex = (int)((mw >> (16 * hf + 10)) & 31u);
-            const int en = (ex > 1 ? ex : 1) - 14;
-            if (en > E[g]) {
-              const float f = ldexpf(1.f, E[g] - en);
-              acc[2 * g] *= f;
-              acc[2 * g + 1] *= f;
-              E[g] = en;
-            }
-          }
-        }
-      }
-      uint32_t rp[GW];
-#pragma unroll
-      for (int w = 0; w < GW; ++w) rp[w] = f16_pow2_neg(E[2 * w]) | (f16_pow2_neg(E[2 * w + 1]) << 16);
-      lds_u16* const vs16 = (lds_u16*)vs;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int d = lane + 64 * k;
-        const int t = d / GW, w = d % GW;
-        uint32_t rpl = rp[0];
-#pragma unroll
-        for (int i = 1; i < GW; ++i)
-          if (w == i) rpl = rp[i];
-        const uint32_t y = pk_mul_f16(x[k], rpl);
-        const int u = 8 * (t & 3) + (t >> 2);
-        const int o = 2 * ((u >> 1) * G + 2 * w) + (u & 1);
-        if (d < C::SC_DW) {
-          vs16[o] = (uint16_t)y;
-          vs16[o + 2] = (uint16_t)(y >> 16);
-        }
-      }
-    }
+    stage_value_scales<D, VB>(sp, full, tl, lane, E, acc, [](int t) { return 8 * (t & 3) + (t >> 2); });
 
     // ---- scores for the two 16-token tiles
     const lds_u16* const ks = (const lds_u16*)(sp + C::OFF_KS);
@@ -877,6 +890,331 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     const int jr = tile * kHeadTile + h;
     const int64_t orow = ((int64_t)b * a.n_queries + jr / rep) * a.n_q_heads + gkv * rep + jr % rep;
+    float* part = a.part + (orow * a.splits + split) * part_stride<D>();
+    part[e] = aa;
+    if (e == 0) {
+      part[D] = mm;
+      part[D + 1] = ll;
+    }
+  }
+}
+
+// All-reduce over the four lane-groups (lanes n, n + 16, n + 32, n + 48):
+// two permlane swaps; every lane gets the same bits (one summation order).
+__device__ __forceinline__ float lg4_max(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+}
+__device__ __forceinline__ float lg4_sum(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
+}
+
+// ----------------------------------------------------------------------------
+// Matrix-core split kernel for many query rows per kv head (several query
+// tokens per sequence, or more than four query heads per kv head).  One block
+// serves 16 (query token, head) rows of one (sequence, kv head, context
+// split), so each cached token is dequantized and scored once for all of
+// them.  The DMA stages, the value-scale normalisation and the PV B operand
+// are those of the kernel above; the contractions are laid out the other
+// way round:
+//  * QK^T on v_mfma_i32_16x16x32_i8, one 32-byte key group per MFMA: A = the
+//    stored key bytes of 16 tokens, B = the 16 rows' fixed-point query (hi
+//    and lo bytes, two MFMAs), so D[4c+i][n] is token 4c+i's group partial
+//    for row n, and the group's key scale and zero apply per element:
+//    s = sum_g scale_g (d_g + zero_g * sum_{j in g} q_j).
+//  * Lane (c, n) then holds row n's scores for tokens 4c+i and 16+4c+i
+//    (i < 4), which are row n's PV A operand at contraction slots 8c .. 8c+7
+//    as they are: p never leaves the registers.  Row statistics are
+//    all-reduced over the four lane-groups with two permlane swaps.
+//  * PV output rows are the 16 rows themselves (no partial sums over token
+//    quarters), so one set of PV MFMAs serves all of them.
+template <int D, int VB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_attn_mfma16_kernel(AttnArgs a) {
+  using C = MfmaCfg<D, VB>;
+  constexpr int G = C::G, NT = C::NT, CH = C::CH, W = C::W, S = C::S;
+  constexpr int R = 16;  // query rows per block
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[C::OFF_BUF + C::BUF];
+  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(lds_all);
+  // the other kernel's p buffers hold the row statistics here
+  static_assert(C::OFF_STATS - C::OFF_PB >= 4 * R * 2 * 4, "row statistics fit");
+  float(*const stats)[R][2] = reinterpret_cast<float(*)[R][2]>(lds_all + C::OFF_PB);
+  uint8_t* const smem = lds_all + C::OFF_BUF;
+
+  const int rep = a.n_q_heads / a.n_kv_heads, nrow = a.n_queries * rep;
+  const int tiles = (nrow + R - 1) / R;
+  int group, tile;
+  if (tiles > 1 && gridDim.x % (8u * tiles) == 0) {
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    tile = j % tiles;
+    group = (j / tiles) * 8 + xcd;
+  } else {
+    tile = (blockIdx.x / a.splits) % tiles;
+    group = (blockIdx.x / a.splits / tiles) * a.splits + blockIdx.x % a.splits;
+  }
+  const int split = group % a.splits;
+  const int rest = group / a.splits;
+  const int gkv = rest % a.n_kv_heads;
+  const int b = rest / a.n_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane >> 4, n = lane & 15;
+  lds_u8* const wbuf = (lds_u8*)smem + wave * S * C::STAGE;
+  lds_u8* const lut = (lds_u8*)lds_all;
+
+  for (int i = threadIdx.x; i < C::LUT; i += blockDim.x) {
+    const uint32_t* cen = attn_centroids<VB>();
+    lut_s[i] = half2_bits(__uint_as_float(cen[i & ((1 << VB) - 1)]), __uint_as_float(cen[i >> VB]));
+  }
+
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  const int t_begin = split * a.tokens_per_split;
+  int t_end = t_begin + a.tokens_per_split;
+  if (t_end > ctx) t_end = ctx;
+  const int64_t row0 = (int64_t)b * a.seq_stride + (int64_t)gkv * a.head_stride;
+
+  const int first = t_begin + wave * CH;
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) {
+    const int cb = first + 4 * CH * k;
+    if (cb + CH <= t_end)
+      attn_dma<D, VB, false>(a, wbuf + k * C::STAGE, row0 + cb, CH, lane);
+    else if (cb < t_end)
+      attn_dma<D, VB, true>(a, wbuf + k * C::STAGE, row0 + cb, t_end - cb, lane);
+  }
+
+  // ---- query row n of the tile: query jr / rep, head jr % rep of this kv head
+  const int jr = tile * R + n;
+  const bool rv = jr < nrow;
+  const int mq = rv ? jr / rep : 0;
+  const uint16_t* const qrow = a.q + (((int64_t)b * a.n_queries + mq) * a.n_q_heads + gkv * rep + (rv ? jr % rep : 0)) * D;
+  // this lane's query elements: 32g + 8c + [0, 8) of every group g
+  uint4 qw[G];
+  float qmax = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qw[g] = rv ? *reinterpret_cast<const uint4*>(qrow + 32 * g + 8 * c) : make_uint4(0, 0, 0, 0);
+    const uint32_t ws[4] = {qw[g].x, qw[g].y, qw[g].z, qw[g].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(ws[i])), fabsf(bf16_hi(ws[i]))));
+  }
+  const float qscale = a.softmax_scale * kLog2e;
+  qmax = lg4_max(qmax) * fabsf(qscale);
+  int qe = 0;
+  (void)frexpf(qmax, &qe);
+  qe = qe < -100 ? -100 : (qe > 100 ? 100 : qe);
+  // fixed point q * softmax_scale * log2 e * 2^(14 - qe), |.| <= 2^14, as the
+  // exact pair hi * 256 + lo (hi in [-64, 64], lo in [-128, 127])
+  const float qn = ldexpf(qscale, 14 - qe);
+  const float smul = ldexpf(1.f, qe - 14);
+  long qh[G], ql[G];
+  float qsum[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint32_t ws[4] = {qw[g].x, qw[g].y, qw[g].z, qw[g].w};
+    uint32_t hw[2] = {0, 0}, lw[2] = {0, 0};
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = (i & 1) ? bf16_hi(ws[i >> 1]) : bf16_lo(ws[i >> 1]);
+      const int v = (int)__builtin_rintf(x * qn);
+      const int lo = ((v + 128) & 255) - 128;
+      const int hi = (v - lo) >> 8;
+      hw[i >> 2] |= (uint32_t)(hi & 255) << (8 * (i & 3));
+      lw[i >> 2] |= (uint32_t)(lo & 255) << (8 * (i & 3));
+      sum += v;
+    }
+    qh[g] = (long)(((uint64_t)hw[1] << 32) | hw[0]);
+    ql[g] = (long)(((uint64_t)lw[1] << 32) | lw[0]);
+    qsum[g] = lg4_sum((float)sum);  // exact: an integer below 2^20
+  }
+  // tokens t < lim are visible to row n
+  int lim = rv ? ctx - a.n_queries + 1 + mq : t_end;
+  if (lim > t_end) lim = t_end;
+  // value fields: as in the kernel above; contraction slot 8c + i is token
+  // 4c + i (i < 4) or 16 + 4c + (i - 4)
+  int fk = (2 * VB * n) >> 5, fsh = (2 * VB * n) & 31;
+  if (fsh < 2) {
+    fk -= 1;
+    fsh += 30;
+  } else {
+    fsh -= 2;
+  }
+  const int vdw = C::OFF_V / 4 + 4 * c * W + fk;
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.f;
+  tq_float4 acc[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = tq_float4{0.f, 0.f, 0.f, 0.f};
+  int E[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) E[g] = -13;
+  const tq_i32x4 zero4 = {0, 0, 0, 0};
+
+  int slot = 0;
+  for (int cb = first; cb < t_end; cb += 4 * CH) {
+    const int cbn = cb + 4 * CH * (S - 1);
+    const int nslot = slot == 0 ? S - 1 : slot - 1;
+    if (cbn + CH <= t_end)
+      attn_dma<D, VB, false>(a, wbuf + nslot * C::STAGE, row0 + cbn, CH, lane);
+    else if (cbn < t_end)
+      attn_dma<D, VB, true>(a, wbuf + nslot * C::STAGE, row0 + cbn, t_end - cbn, lane);
+    const int later = (t_end - cb - 1) / (4 * CH);
+    if (later >= 2 && S == 3)
+      wait_vmcnt<(S - 1) * C::NI>();
+    else if (later >= 1)
+      wait_vmcnt<C::NI>();
+    else
+      wait_vmcnt<0>();
+
+    lds_u8* const sp = wbuf + slot * C::STAGE;
+    slot = slot == S - 1 ? 0 : slot + 1;
+    const int tl = t_end - cb;
+    const bool full = tl >= CH;
+
+    stage_value_scales<D, VB>(sp, full, tl, lane, E, acc,
+                              [](int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); });
+
+    // ---- scores: lane (c, n) gets row n at tokens 16 tau + 4c + i
+    const lds_u16* const ks = (const lds_u16*)(sp + C::OFF_KS);
+    const lds_u16* const kz = (const lds_u16*)(sp + C::OFF_KZ);
+    float P[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int tk = 16 * tau + n;  // the A operand's token
+      const int t0 = 16 * tau + 4 * c;
+      float T[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int ch = 2 * g + (c >> 1);
+        const long kw = *(const __attribute__((address_space(3))) long*)(
+            sp + 16 * (tk * C::CPR + (ch ^ (tk & (C::SW - 1)))) + 8 * (c & 1));
+        const tq_i32x4 dh = __builtin_amdgcn_mfma_i32_16x16x32_i8(kw, qh[g], zero4, 0, 0, 0);
+        const tq_i32x4 dl = __builtin_amdgcn_mfma_i32_16x16x32_i8(kw, ql[g], zero4, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sk = f16_value(ks[(t0 + i) * G + g]);
+          const float zk = f16_value(kz[(t0 + i) * G + g]);
+          const float d = (float)(dh[i] * 256 + dl[i]);
+          T[i] = __builtin_fmaf(sk, __builtin_fmaf(zk, qsum[g], d), T[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) P[tau][i] = (cb + t0 + i < lim) ? T[i] * smul : -INFINITY;
+    }
+    // ---- online softmax of row n (lazy running maximum, as above)
+    float cm = P[0][0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) cm = fmaxf(cm, P[k >> 2][k & 3]);
+    cm = lg4_max(cm);
+    const float m_new = (cm > m_run + kLazy) ? cm : m_run;
+    float alpha = 1.f;
+    if (m_new != -INFINITY) {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) P[k >> 2][k & 3] = __builtin_amdgcn_exp2f(P[k >> 2][k & 3] - m_new);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) P[k >> 2][k & 3] = 0.f;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ps += P[k >> 2][k & 3];
+    l_run = l_run * alpha + lg4_sum(ps);
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+      // accumulator row 4c + i belongs to the lanes n = 4c + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * c + i);
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) acc[jt][i] *= ai;
+      }
+    }
+
+    // ---- PV.  A: p of row n at slots 8c .. 8c+7 times the normalised value
+    // scales of those tokens; B: the centroids of those tokens at this lane's
+    // two dims (as in the kernel above)
+    const uint32_t ph[4] = {half2_bits(P[0][0], P[0][1]), half2_bits(P[0][2], P[0][3]),
+                            half2_bits(P[1][0], P[1][1]), half2_bits(P[1][2], P[1][3])};
+    const lds_u32* const vsn = (const lds_u32*)(sp + C::OFF_VS) + 4 * c * G;
+    uint32_t sv[4][G];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int g = 0; g < G; ++g) sv[k][g] = vsn[k * G + g];
+    uint32_t va0 = lds_addr(sp) + 4u * (uint32_t)vdw, va1 = va0 + 64u * W;
+    asm volatile("" : "+v"(va0), "+v"(va1));
+    const lds_u32* const vrow0 = (const lds_u32*)(uintptr_t)va0;
+    const lds_u32* const vrow1 = (const lds_u32*)(uintptr_t)va1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      uint32_t aw[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) aw[k2] = pk_mul_f16(ph[k2], sv[k2][g]);
+      uint32_t L[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const lds_u32* f = (i < 4 ? vrow0 : vrow1) + W * (i & 3) + VB * g;
+        const uint32_t x = __builtin_amdgcn_alignbit(f[1], f[0], (uint32_t)fsh);
+        L[i] = *(const lds_u32*)(lut + (x & ((uint32_t)(C::LUT - 1) << 2)));
+      }
+      uint32_t b0[4], b1[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        b0[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x05040100u);
+        b1[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x07060302u);
+      }
+      const tq_half8 ap = __builtin_bit_cast(tq_half8, aw);
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(tq_half8, b0), acc[2 * g], 0, 0, 0);
+      acc[2 * g + 1] =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(tq_half8, b1), acc[2 * g + 1], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- back to true scale, merge the waves, write the split partials
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float f = ldexpf(1.f, E[g]);
+    acc[2 * g] *= f;
+    acc[2 * g + 1] *= f;
+  }
+  if (c == 0) {
+    stats[wave][n][0] = m_run;
+    stats[wave][n][1] = l_run;
+  }
+  __syncthreads();
+  lds_f32* const accb = (lds_f32*)smem;
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) accb[((wave * NT + jt) * 4 + i) * 64 + lane] = acc[jt][i];
+  __syncthreads();
+  for (int o = threadIdx.x; o < R * D; o += blockDim.x) {
+    const int h = o / D, e = o % D;
+    const int jh = tile * R + h;
+    if (jh >= nrow) continue;
+    float mm = -INFINITY;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, stats[w][h][0]);
+    float ll = 0.f, aa = 0.f;
+    if (mm != -INFINITY) {
+      // dim e = 32g + 2nn + jj sits in tile 2g + jj, column nn; row h is
+      // register h % 4 of lane-group h / 4
+      const int jt = 2 * (e >> 5) + (e & 1), nn = (e & 31) >> 1;
+      for (int w = 0; w < 4; ++w) {
+        const float f = exp2f(stats[w][h][0] - mm);
+        ll += stats[w][h][1] * f;
+        aa += accb[((w * NT + jt) * 4 + (h & 3)) * 64 + 16 * (h >> 2) + nn] * f;
+      }
+    }
+    const int64_t orow = ((int64_t)b * a.n_queries + jh / rep) * a.n_q_heads + gkv * rep + jh % rep;
     float* part = a.part + (orow * a.splits + split) * part_stride<D>();
     part[e] = aa;
     if (e == 0) {
@@ -1051,8 +1389,11 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   // matrix-core path, four waves of kChunk rows per lane-group otherwise
   const bool mfma = decode_attn_uses_mfma(d, kb, vb);
   const int step = mfma ? 4 * 32 : 4 * (64 / (d / 8)) * kChunk;
-  const int rep = n_q_heads / n_kv_heads;
-  const long long units = (long long)batch * n_kv_heads * ((n_queries * rep + kHeadTile - 1) / kHeadTile);
+  const int rep = n_q_heads / n_kv_heads, nrow = n_queries * rep;
+  // query rows per block: 16 on the matrix-core path once a kv head has more
+  // than one tile of four
+  const int rows = mfma && nrow > kHeadTile ? 16 : kHeadTile;
+  const long long units = (long long)batch * n_kv_heads * ((nrow + rows - 1) / rows);
   // The matrix-core kernel streams through per-wave DMA stages, which pay a
   // pipeline fill per block: aim at one round of resident blocks (two per CU
   // on the 256 CUs of gfx950).  The VALU kernel prefers more, shorter blocks.
@@ -1102,11 +1443,23 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
       AttnArgs w = a;
       w.wide = ((uintptr_t)a.v_q & 15u) == 0 && ((uintptr_t)a.k_scale & 15u) == 0 &&
                ((uintptr_t)a.k_zero & 15u) == 0 && (a.seq_stride & 1) == 0 && (a.head_stride & 1) == 0;
-      switch (vb) {
-        case 2: decode_attn_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(w); break;
-        case 3: decode_attn_mfma_kernel<D, 3><<<grid, 256, 0, st>>>(w); break;
-        case 4: decode_attn_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(w); break;
-        default: decode_attn_mfma_kernel<D, 5><<<grid, 256, 0, st>>>(w); break;
+      const int nrow = a.n_queries * rep;
+      if (nrow > kHeadTile) {
+        // 16 (query, head) rows per block
+        const dim3 g16((unsigned)(a.batch * a.n_kv_heads * ((nrow + 15) / 16) * a.splits));
+        switch (vb) {
+          case 2: decode_attn_mfma16_kernel<D, 2><<<g16, 256, 0, st>>>(w); break;
+          case 3: decode_attn_mfma16_kernel<D, 3><<<g16, 256, 0, st>>>(w); break;
+          case 4: decode_attn_mfma16_kernel<D, 4><<<g16, 256, 0, st>>>(w); break;
+          default: decode_attn_mfma16_kernel<D, 5><<<g16, 256, 0, st>>>(w); break;
+        }
+      } else {
+        switch (vb) {
+          case 2: decode_attn_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(w); break;
+          case 3: decode_attn_mfma_kernel<D, 3><<<grid, 256, 0, st>>>(w); break;
+          case 4: decode_attn_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(w); break;
+          default: decode_attn_mfma_kernel<D, 5><<<grid, 256, 0, st>>>(w); break;
+        }
       }
       launch_combine<D>(a, st);
       return hipGetLastError();

@@ -162,10 +162,11 @@ def test_full_size_decode_pairs():
     _say(f"[gpu attn] full size decode: {len(pairs)} pairs, ties k={kt} v={vt}, worst {worst}")
 
 
-def run_mq_case(B, M, Hq, Hkv, N, d, kb, vb, ctx, seed, tag):
+def run_mq_case(B, M, Hq, Hkv, N, d, kb, vb, ctx, seed, tag, k_mul=1.0, v_mul=1.0, q_mul=1.0):
     _say(f"[gpu attn] multi-query {tag}: B={B} M={M} Hq={Hq} Hkv={Hkv} N={N} d={d} k{kb}v{vb} ctx={ctx}")
     k, v = synth.kv_inputs("normal", B, N, Hkv, d, seed)
     q = synth.queries(B * M, Hq, d, seed + 7).reshape(B, M, Hq, d)
+    k, v, q = _scaled(k, k_mul), _scaled(v, v_mul), _scaled(q, q_mul)
     signs = synth.sign_vector(d)
     sig = torch.from_numpy(signs).to(DEV)
     cache = tq.quantize_into_cache(k.to(DEV), v.to(DEV), sig, kb, vb)
@@ -195,6 +196,33 @@ def test_multi_query_causal(M):
 def test_gqa6_d256(M):
     # the pages' research attention shape: GQA 6 at head_dim 256
     run_mq_case(2, M, 12, 2, 400, 256, 8, 3, [400, 257], 19, f"gqa6 d256 M{M}")
+
+
+# More than four (query, head) rows per kv head run 16 rows per block, so a
+# cached token is scored once for all of them.  Row counts below, at and above
+# one tile, idle rows, a sequence shorter than the query chunk, many splits.
+@pytest.mark.parametrize("B,M,Hq,Hkv,N,d,vb,ctx", [
+    (2, 1, 16, 2, 300, 128, 3, [300, 171]),      # rep 8, one query: 8 rows
+    (2, 1, 10, 2, 300, 128, 3, [300, 45]),       # rep 5: 5 rows
+    (2, 4, 16, 4, 520, 128, 5, [520, 250]),      # 16 rows, 5-bit values
+    (2, 8, 8, 4, 400, 128, 3, [400, 5]),         # 16 rows; the second sequence's first queries see nothing
+    (1, 9, 8, 4, 700, 64, 2, [700]),             # 18 rows: two tiles, the second ragged
+    (2, 3, 24, 4, 260, 256, 4, [260, 255]),      # rep 6 x 3 queries = 18 rows at d256
+    (1, 4, 32, 8, 9000, 128, 3, [9000]),         # many splits
+])
+def test_sixteen_row_tiles(B, M, Hq, Hkv, N, d, vb, ctx):
+    got, ref = run_mq_case(B, M, Hq, Hkv, N, d, 8, vb, ctx, 24, f"16-row tiles M{M} rep{Hq // Hkv} d{d} v{vb}")
+    for b, c in enumerate(ctx):
+        for m in range(M):
+            if c - M + m + 1 <= 0:
+                assert not got[b, m].any()
+
+
+@pytest.mark.parametrize("k_mul,v_mul,q_mul", [(1.0, 1e-6, 1.0), (1e-5, 1.0, 2e5), (1.0, 1.0, 1e-3),
+                                               (1.0, 300.0, 1.0)])
+def test_sixteen_row_magnitudes(k_mul, v_mul, q_mul):
+    run_mq_case(2, 4, 8, 2, 400, 128, 8, 3, [400, 233], 25, f"16-row k*{k_mul} v*{v_mul} q*{q_mul}",
+                k_mul, v_mul, q_mul)
 
 
 def test_multi_query_valu_schemes():
