@@ -29,6 +29,9 @@
  *   v_q are 8-byte aligned; the fp16 planes are 2-byte aligned.  Plane row
  *   lengths keep these for any row offset.  Input and output buffers must
  *   not overlap.
+ * - Counts: a codec or cache call serves fewer than 2^31 rows, each count
+ *   of a tq_rows below 2^31; an attention call fewer than 2^30 query rows
+ *   (batch x queries x query heads).  Larger calls are TQ_E_SHAPE.
  * - Validation runs on the host before any launch; on error nothing is
  *   launched and a negative TQ_E_* code is returned.  Zero rows is a no-op.
  *   Device faults surface at the caller's next synchronisation.

@@ -57,6 +57,9 @@ int32_t check_rows(const tq_rows* r, uint32_t* rows, tq::RowSplit* split) {
   if (!r) return TQ_E_NULL;
   if (r->n_seq < 0 || r->n_tok < 0 || r->n_head < 0) return TQ_E_SHAPE;
   if (r->seq_stride < 0 || r->tok_stride < 0 || r->head_stride < 0) return TQ_E_SHAPE;
+  // each count below 2^31 first, so that the product (at most 93 bits) is exact
+  const int64_t lim = (int64_t)1 << 31;
+  if (r->n_seq >= lim || r->n_tok >= lim || r->n_head >= lim) return TQ_E_SHAPE;
   const unsigned __int128 n = (unsigned __int128)r->n_seq * r->n_tok * r->n_head;
   if (n >= ((unsigned __int128)1 << 31)) return TQ_E_SHAPE;
   *rows = (uint32_t)n;
@@ -341,6 +344,10 @@ int32_t tq_grow_kv(const tq_scheme* s, int32_t batch, int32_t n_kv_heads, const 
     return TQ_E_SHAPE;
   if (batch == 0 || n_kv_heads == 0 || dst_capacity == 0) return TQ_OK;
   const int64_t keep = src_capacity < dst_capacity ? src_capacity : dst_capacity;
+  // an axis of extent 1 never steps, so its stride plays no part (and is not
+  // multiplied out below: the byte spans bound every product that is)
+  const int64_t sss = batch > 1 ? src_seq_stride_rows : 0, shs = n_kv_heads > 1 ? src_head_stride_rows : 0;
+  const int64_t dss = batch > 1 ? dst_seq_stride_rows : 0, dhs = n_kv_heads > 1 ? dst_head_stride_rows : 0;
   const void* sp[5] = {src->k_q, src->k_scale, src->k_zero, src->v_q, src->v_scale};
   void* dp[5] = {dst->k_q, dst->k_scale, dst->k_zero, dst->v_q, dst->v_scale};
   Span rd[5], wr[5];
@@ -348,17 +355,16 @@ int32_t tq_grow_kv(const tq_scheme* s, int32_t batch, int32_t n_kv_heads, const 
   uint64_t total = 0;
   for (int p = 0; p < 5; ++p) {
     const int64_t rb = tq_plane_row_bytes(s, p);
-    if (!plane_span(sp[p], rb, batch, n_kv_heads, src_seq_stride_rows, src_head_stride_rows, keep, &rd[p]) ||
-        !plane_span(dp[p], rb, batch, n_kv_heads, dst_seq_stride_rows, dst_head_stride_rows, dst_capacity,
-                    &wr[p]))
+    if (!plane_span(sp[p], rb, batch, n_kv_heads, sss, shs, keep, &rd[p]) ||
+        !plane_span(dp[p], rb, batch, n_kv_heads, dss, dhs, dst_capacity, &wr[p]))
       return TQ_E_SHAPE;
     tq::GrowPlane& g = a.plane[p];
     g.src = (const uint8_t*)sp[p];
     g.dst = (uint8_t*)dp[p];
-    g.src_seq = src_seq_stride_rows * rb;
-    g.src_head = src_head_stride_rows * rb;
-    g.dst_seq = dst_seq_stride_rows * rb;
-    g.dst_head = dst_head_stride_rows * rb;
+    g.src_seq = sss * rb;
+    g.src_head = shs * rb;
+    g.dst_seq = dss * rb;
+    g.dst_head = dhs * rb;
     g.copy = keep * rb;
     g.dst_bytes = (int64_t)dst_capacity * rb;
     const uint64_t chunks = (uint64_t)((g.dst_bytes + tq::kGrowChunkBytes - 1) / tq::kGrowChunkBytes);
@@ -405,7 +411,8 @@ size_t tq_attn_quant_workspace_bytes(const tq_scheme* s, int32_t batch, int32_t 
   if (check_scheme(s) != TQ_OK) return 0;
   if (batch < 0 || n_queries < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1)
     return 0;
-  if ((int64_t)batch * n_queries * n_q_heads >= ((int64_t)1 << 31)) return 0;
+  if ((__int128)batch * n_queries * n_q_heads >= ((__int128)1 << 30)) return 0;
+  if (batch == 0) return 0;  // nothing runs
   int splits = 0, tps = 0;
   tq::decode_attn_geometry(s->head_dim, s->k_bits, s->v_bits, batch, n_queries, n_q_heads, n_kv_heads, max_ctx,
                            &splits, &tps);
@@ -433,7 +440,9 @@ int32_t attn_prepare(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, 
   if (batch < 0 || n_queries < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || max_ctx < 1 ||
       seq_stride_rows < 0 || head_stride_rows < 0)
     return TQ_E_SHAPE;
-  if ((int64_t)batch * n_queries * n_q_heads >= ((int64_t)1 << 31)) return TQ_E_SHAPE;
+  // below 2^30 query rows, so that no row or tile count in the launch arithmetic
+  // (int32 on host and device) comes near overflow
+  if ((__int128)batch * n_queries * n_q_heads >= ((__int128)1 << 30)) return TQ_E_SHAPE;
   *a = tq::AttnArgs{};
   *need = 0;
   if (batch == 0) return TQ_OK;

@@ -1389,11 +1389,12 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   // matrix-core path, four waves of kChunk rows per lane-group otherwise
   const bool mfma = decode_attn_uses_mfma(d, kb, vb);
   const int step = mfma ? 4 * 32 : 4 * (64 / (d / 8)) * kChunk;
-  const int rep = n_q_heads / n_kv_heads, nrow = n_queries * rep;
+  const long long rep = n_q_heads / n_kv_heads, nrow = (long long)n_queries * rep;
   // query rows per block: 16 on the matrix-core path once a kv head has more
   // than one tile of four
-  const int rows = mfma && nrow > kHeadTile ? 16 : kHeadTile;
-  const long long units = (long long)batch * n_kv_heads * ((nrow + rows - 1) / rows);
+  const long long rows = mfma && nrow > kHeadTile ? 16 : kHeadTile;
+  long long units = (long long)batch * n_kv_heads * ((nrow + rows - 1) / rows);
+  if (units < 1) units = 1;  // an empty batch: nothing runs, any split count serves
   // The matrix-core kernel streams through per-wave DMA stages, which pay a
   // pipeline fill per block: aim at one round of resident blocks (two per CU
   // on the 256 CUs of gfx950).  The VALU kernel prefers more, shorter blocks.
