@@ -1400,12 +1400,19 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   // on the 256 CUs of gfx950).  The VALU kernel prefers more, shorter blocks.
   // Each split of the matrix-core kernel also keeps at least four steps per
   // wave, so that the fill is paid over several steps and the combine does
-  // not merge dozens of tiny splits (one sequence, 4 kv heads, 16384 tokens
-  // at d = 256: 64 splits of 2 steps took 47 us, 32 of 4 take 33 us).
+  // not merge dozens of tiny splits, but only while the grid still has 256
+  // blocks: a short launch-bound decode does better with more parallel blocks
+  // of a step or two (one sequence, 8 kv heads, d = 128: 17.8 -> 13.5 us at
+  // 2048 tokens, 18.6 -> 17.0 us at 8192; GQA 6 at d = 256 over 16384 tokens,
+  // one 16-row tile per kv head: 32.5 -> 28.4 us).
   const long long target = mfma ? 512 : 2048;
   const long long min_steps = mfma ? 4 : 1;
   long long s = (target + units - 1) / units;
-  const long long max_s = (max_ctx + min_steps * step - 1) / (min_steps * step);
+  long long max_s = (max_ctx + min_steps * step - 1) / (min_steps * step);
+  if (units * max_s < 256) {
+    const long long fill = (256 + units - 1) / units, one_step = (max_ctx + step - 1) / step;
+    max_s = fill < one_step ? fill : one_step;
+  }
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   long long tps = (max_ctx + s - 1) / s;
