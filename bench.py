@@ -332,9 +332,24 @@ def measure_latency(tq, synth, dev):
         for kl, vl, pll in per_layer:
             tq.quantize_kv(kl, vl, sig, kb, vb, out=pll)
     us_64 = _time_us(layers, 20)
+    # the same 64 launches captured once in a HIP graph and replayed: the GPU
+    # side of per-layer calls, without the host's per-call cost
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layers()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        layers()
+    us_64g = _time_us(graph.replay, 50)
+    del graph
     rows = L * T * H
     for tag, u, what in (("one_launch", us_one, "one launch over all rows"),
-                         ("per_layer_launches", us_64, f"{L} per-layer launches of {T * H} rows")):
+                         ("per_layer_launches", us_64, f"{L} per-layer launches of {T * H} rows"),
+                         ("per_layer_launches_graph", us_64g,
+                          f"{L} per-layer launches of {T * H} rows, replayed from a captured HIP graph")):
         out[f"decode_append_step_{tag}"] = {"workload": f"decode append k{kb}v{vb} d{d}: {L}x{T}x{H} rows, {what}",
                                             "us": u, "token_heads_per_s": rows / (u * 1e-6)}
     # d512 k5v2, one layer
