@@ -12,9 +12,9 @@ import torch
 
 from kv_cache_quantization_02_amd import binding as tq
 from kv_cache_quantization_02_amd import synth
+from oracle import attention, codec
 from oracle import cache as oc
-from oracle import codec
-from parity import compare_planes
+from parity import attention_close, compare_planes
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -233,6 +233,22 @@ def test_appends_across_growth_boundaries():
         torch.cuda.synchronize()
         Kr, Vr = oc.fetch_kv(got, lens, 768, signs, d, kb, vb, values_rotated=rotated)
         assert np.array_equal(synth.bf16_bits(K), Kr) and np.array_equal(synth.bf16_bits(V), Vr)
+    # attention over the grown cache: the same launch as over the one-shot cache
+    # (same capacity), and the oracle's attention over the cached rows
+    Hq = 4 * H
+    q = synth.queries(B, Hq, d, 41)
+    a_grown = tq.decode_attn(q.to(DEV), cache, L, sig, kb, vb, H)
+    a_big = tq.decode_attn(q.to(DEV), big, L, sig, kb, vb, H)
+    torch.cuda.synchronize()
+    assert torch.equal(a_grown.view(torch.int16), a_big.view(torch.int16))
+    rows = {name: got[name].reshape(B * H * 768, -1) for name in tq.PLANES}
+    khat = codec.dequantize_keys_f32(codec.key_indices(rows["k_q"], kb, d), rows["k_scale"], rows["k_zero"])
+    z = codec.dequantize_values_rotated_f32(codec.unpack_bits(rows["v_q"], vb, d).astype(np.int32),
+                                            rows["v_scale"], vb)
+    ref = attention.decode_attention(codec.bf16_to_f32(synth.bf16_bits(q)), khat.reshape(B, H, 768, d),
+                                     z.reshape(B, H, 768, d), signs, lens, np.float32(1 / np.sqrt(d)))
+    st = attention_close(synth.bf16_bits(a_grown).reshape(B, Hq, d), ref)
+    _say(f"[gpu cache] attention over the grown cache: {st}")
 
 
 def test_grow_full_size_decode_cache():
