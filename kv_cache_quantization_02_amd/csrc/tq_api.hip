@@ -25,9 +25,11 @@ const uint32_t kCen8[] = {TQ_CENTROIDS_8BIT}, kBnd8[] = {TQ_BOUNDARIES_8BIT};
 #endif
 constexpr int kMaxCodecBlocks = TQ_MAX_CODEC_BLOCKS;
 
-// Cap on the blocks of a cache re-lay; a grid-stride loop covers the rest.
+// Cap on the blocks of a cache re-lay (16 KB each); a grid-stride loop covers
+// the rest.  32768 was 2% faster than 8192 on the 1.7 GB growth of the decode
+// cache, and as fast as 65536.
 #ifndef TQ_MAX_GROW_BLOCKS
-#define TQ_MAX_GROW_BLOCKS 8192
+#define TQ_MAX_GROW_BLOCKS 32768
 #endif
 constexpr int kMaxGrowBlocks = TQ_MAX_GROW_BLOCKS;
 
