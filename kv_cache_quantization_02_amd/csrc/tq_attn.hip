@@ -333,13 +333,14 @@ __device__ __forceinline__ uint32_t f16_pow2_neg(int e) {
   return e <= 14 ? (uint32_t)(15 - e) << 10 : 1u << (24 - e);
 }
 
-template <int D, int VB>
+template <int D, int KB, int VB>
 struct MfmaCfg {
   static constexpr int G = D / kGroup, GW = G / 2, NSET = (G + 3) / 4, NT = D / 16, CH = 32;
-  static constexpr int CPR = D / 16, SW = CPR < 8 ? CPR : 8;  // key chunks per row, swizzle span
+  static constexpr int KRB = KB == 8 ? D : D * KB / 8;       // key row bytes
+  static constexpr int CPR = KRB / 16, SW = CPR < 8 ? CPR : 8;  // key chunks per row, swizzle span
   static constexpr int W = D * VB / 32;                      // packed value dwords per row
   static constexpr int RB = 4 * W;                           // packed value bytes per row
-  static constexpr int NK = CH * D / 1024;                   // 16-byte DMAs of key rows
+  static constexpr int NK = CH * KRB / 1024;                 // 16-byte DMAs of key rows
   static constexpr int NV = CH * W / 64;                     // 4-byte DMAs of value rows
   static constexpr int SC_DW = CH * GW, NSP = (SC_DW + 63) / 64;  // per fp16 plane
   static constexpr int NI_TAIL = NK + NV + 3 * NSP;          // DMA instructions of a partial step
@@ -351,7 +352,7 @@ struct MfmaCfg {
   static constexpr int NVW = (CH * RB + 1023) / 1024;        // 16-byte DMAs of values (+ key planes)
   static constexpr int NI_FULL = WIDE ? NK + NVW + NSP : NI_TAIL;
   static constexpr int NI = NI_FULL < NI_TAIL ? NI_FULL : NI_TAIL;  // fewest per step (the waits count these)
-  static constexpr int OFF_V = CH * D;
+  static constexpr int OFF_V = CH * KRB;
   static constexpr int OFF_KS = OFF_V + CH * RB;
   static constexpr int OFF_KZ = OFF_KS + NSP * 256;
   static constexpr int OFF_VS = OFF_KZ + NSP * 256;
@@ -366,7 +367,7 @@ struct MfmaCfg {
   static constexpr int S = (4 * 3 * STAGE + EXTRA <= 81920 && 2 * NI_TAIL <= 63) ? 3 : 2;
   static constexpr int ACC_BYTES = 4 * NT * 4 * 64 * 4;
   static constexpr int BUF = (4 * S * STAGE > ACC_BYTES) ? 4 * S * STAGE : ACC_BYTES;
-  static_assert(G % 2 == 0 && (CH * W) % 64 == 0 && (CH * D) % 1024 == 0, "step layout");
+  static_assert(G % 2 == 0 && (CH * W) % 64 == 0 && (CH * KRB) % 1024 == 0, "step layout");
   static_assert((S - 1) * NI_TAIL <= 63, "vmcnt range");
 };
 
@@ -390,19 +391,61 @@ __device__ __forceinline__ void dma_x4_addr(const void* addr, uint32_t lds) {
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 
+// Key indices as MFMA operand bytes.  int8 keys are the stored bytes; packed
+// unsigned 4- and 2-bit keys are spread into bytes in an order of their own
+// (no shuffling), and the query operand is built in the same order
+// (key_elem*: the element held at operand byte i), which leaves the
+// contraction unchanged.  The fields of a little-endian stream sit at bit
+// KB * e of its words.
+template <int KB>
+constexpr int key_elem16(int i) {
+  return KB == 8 ? i : KB == 4 ? ((i >> 3) << 3) + 2 * (i & 3) + ((i >> 2) & 1) : 4 * (i & 3) + (i >> 2);
+}
+template <int KB>
+constexpr int key_elem8(int i) {
+  return KB == 8 ? i : 2 * (i & 3) + (i >> 2);
+}
+// 16 indices from the bytes at p (16, 8 or 4 of them)
+template <int KB>
+__device__ __forceinline__ tq_i32x4 keys16(const lds_u8* p) {
+  if constexpr (KB == 8) {
+    return *(const lds_i32x4*)p;
+  } else if constexpr (KB == 4) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)p;
+    const uint32_t m = 0x0F0F0F0Fu;
+    return tq_i32x4{(int)(w.x & m), (int)((w.x >> 4) & m), (int)(w.y & m), (int)((w.y >> 4) & m)};
+  } else {
+    static_assert(KB == 2, "packed keys of 4 or 2 bits");
+    const uint32_t w = *(const lds_u32*)p, m = 0x03030303u;
+    return tq_i32x4{(int)(w & m), (int)((w >> 2) & m), (int)((w >> 4) & m), (int)((w >> 6) & m)};
+  }
+}
+// 8 indices from the bytes at p (8 or 4 of them)
+template <int KB>
+__device__ __forceinline__ long keys8(const lds_u8* p) {
+  if constexpr (KB == 8) {
+    return *(const __attribute__((address_space(3))) long*)p;
+  } else {
+    static_assert(KB == 4, "the sixteen-row kernel takes 8- and 4-bit keys");
+    const uint32_t w = *(const lds_u32*)p, m = 0x0F0F0F0Fu;
+    return (long)(((uint64_t)((w >> 4) & m) << 32) | (w & m));
+  }
+}
+
 // Issue the DMAs of the step whose first row is r0 into `stage`.  TAIL: only
 // the first tl rows are inside the context; later rows re-read row tl - 1.
-template <int D, int VB, bool TAIL>
+template <int D, int KB, int VB, bool TAIL>
 __device__ __forceinline__ void attn_dma(const AttnArgs& a, lds_u8* stage, int64_t r0, int tl, int lane) {
-  using C = MfmaCfg<D, VB>;
-  const uint8_t* kb = a.k_q + r0 * D;
+  using C = MfmaCfg<D, KB, VB>;
+  const uint8_t* kb = a.k_q + r0 * C::KRB;
 #pragma unroll
   for (int j = 0; j < C::NK; ++j) {
     const int s = 64 * j + lane;
     int t = s / C::CPR;
     const int ch = (s % C::CPR) ^ (t & (C::SW - 1));
     if (TAIL) t = min(t, tl - 1);
-    dma_x4(kb, (uint32_t)(t * D + 16 * ch), lds_addr(stage + 1024 * j));
+    dma_x4(kb, (uint32_t)(t * C::KRB + 16 * ch), lds_addr(stage + 1024 * j));
   }
   if (C::WIDE && !TAIL && a.wide) {
     // value rows, then (upper lanes of the last copy) the key scale and zero planes
@@ -466,10 +509,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // contraction slots (dword (slot / 2) * G + g holds slots 2k, 2k + 1 of
 // group g), multiplied by 2^-E_g, so that the PV A operand reads them as they
 // are.  slot_of(t) is token t's contraction slot.
-template <int D, int VB, typename SlotOf>
+template <int D, int KB, int VB, typename SlotOf>
 __device__ __forceinline__ void stage_value_scales(lds_u8* sp, bool full, int tl, int lane, int (&E)[D / kGroup],
                                                    tq_float4 (&acc)[D / 16], SlotOf slot_of) {
-  using C = MfmaCfg<D, VB>;
+  using C = MfmaCfg<D, KB, VB>;
   constexpr int G = C::G, GW = C::GW;
   lds_u32* const vs = (lds_u32*)(sp + C::OFF_VS);
   constexpr int PER = (C::SC_DW + 63) / 64;
@@ -540,9 +583,9 @@ __device__ __forceinline__ void stage_value_scales(lds_u8* sp, bool full, int tl
   }
 }
 
-template <int D, int VB>
+template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_attn_mfma_kernel(AttnArgs a) {
-  using C = MfmaCfg<D, VB>;
+  using C = MfmaCfg<D, KB, VB>;
   constexpr int G = C::G, GW = C::GW, NSET = C::NSET, NT = C::NT, CH = C::CH, W = C::W, S = C::S;
   // one LDS block: the centroid-pair table first (its byte offsets are the
   // masked index bits themselves), then p, the merge statistics, the stages
@@ -598,9 +641,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   for (int k = 0; k < S - 1; ++k) {
     const int cb = first + 4 * CH * k;
     if (cb + CH <= t_end)
-      attn_dma<D, VB, false>(a, wbuf + k * C::STAGE, row0 + cb, CH, lane);
+      attn_dma<D, KB, VB, false>(a, wbuf + k * C::STAGE, row0 + cb, CH, lane);
     else if (cb < t_end)
-      attn_dma<D, VB, true>(a, wbuf + k * C::STAGE, row0 + cb, t_end - cb, lane);
+      attn_dma<D, KB, VB, true>(a, wbuf + k * C::STAGE, row0 + cb, t_end - cb, lane);
   }
 
   // ---- query
@@ -657,7 +700,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float x = (i & 1) ? bf16_hi(ws[i >> 1]) : bf16_lo(ws[i >> 1]);
+      const int e = key_elem16<KB>(i);  // the key operand's element at byte i
+      const float x = (e & 1) ? bf16_hi(ws[e >> 1]) : bf16_lo(ws[e >> 1]);
       const int v = qfix(x * qn_l);
       const int lo = ((v + 128) & 255) - 128;
       const int hi = (v - lo) >> 8;
@@ -714,9 +758,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int cbn = cb + 4 * CH * (S - 1);
     const int nslot = slot == 0 ? S - 1 : slot - 1;
     if (cbn + CH <= t_end)
-      attn_dma<D, VB, false>(a, wbuf + nslot * C::STAGE, row0 + cbn, CH, lane);
+      attn_dma<D, KB, VB, false>(a, wbuf + nslot * C::STAGE, row0 + cbn, CH, lane);
     else if (cbn < t_end)
-      attn_dma<D, VB, true>(a, wbuf + nslot * C::STAGE, row0 + cbn, t_end - cbn, lane);
+      attn_dma<D, KB, VB, true>(a, wbuf + nslot * C::STAGE, row0 + cbn, t_end - cbn, lane);
     const int later = (t_end - cb - 1) / (4 * CH);  // steps after this one
     if (later >= 2 && S == 3)
       wait_vmcnt<(S - 1) * C::NI>();
@@ -733,7 +777,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // ---- value scales: zero rows past the context, track E_g, normalise,
     // and rewrite them in place as fp16 pairs (slot 2k, slot 2k+1) per group,
     // slot 8 (t mod 4) + t / 4 for token t: the A operand of PV reads them as is
-    stage_value_scales<D, VB>(sp, full, tl, lane, E, acc, [](int t) { return 8 * (t & 3) + (t >> 2); });
+    stage_value_scales<D, KB, VB>(sp, full, tl, lane, E, acc, [](int t) { return 8 * (t & 3) + (t >> 2); });
 
     // ---- scores for the two 16-token tiles
     const lds_u16* const ks = (const lds_u16*)(sp + C::OFF_KS);
@@ -750,8 +794,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         for (int gq = 0; gq < 2; ++gq) {
           const int gp = 2 * st + gq;
           if (gp < G / 2) {
-            const int ch = 4 * gp + c;
-            const tq_i32x4 kw = *(const lds_i32x4*)(sp + 16 * (t * C::CPR + (ch ^ (t & (C::SW - 1)))));
+            // this lane's 16 key indices: elements 64 gp + 16 c .. + 15 of the row
+            constexpr int BO = 16 * KB / 8;  // their packed bytes
+            const int bo = (4 * gp + c) * BO, ch = bo >> 4;
+            const tq_i32x4 kw = keys16<KB>(sp + 16 * (t * C::CPR + (ch ^ (t & (C::SW - 1)))) + (bo & 15));
             dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(aqh[gp], kw, dh, 0, 0, 0);
             dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(aql[gp], kw, dl, 0, 0, 0);
           }
@@ -933,9 +979,9 @@ __device__ __forceinline__ float lg4_sum(float v) {
 //    all-reduced over the four lane-groups with two permlane swaps.
 //  * PV output rows are the 16 rows themselves (no partial sums over token
 //    quarters), so one set of PV MFMAs serves all of them.
-template <int D, int VB>
+template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_attn_mfma16_kernel(AttnArgs a) {
-  using C = MfmaCfg<D, VB>;
+  using C = MfmaCfg<D, KB, VB>;
   constexpr int G = C::G, NT = C::NT, CH = C::CH, W = C::W, S = C::S;
   constexpr int R = 16;  // query rows per block
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[C::OFF_BUF + C::BUF];
@@ -983,9 +1029,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   for (int k = 0; k < S - 1; ++k) {
     const int cb = first + 4 * CH * k;
     if (cb + CH <= t_end)
-      attn_dma<D, VB, false>(a, wbuf + k * C::STAGE, row0 + cb, CH, lane);
+      attn_dma<D, KB, VB, false>(a, wbuf + k * C::STAGE, row0 + cb, CH, lane);
     else if (cb < t_end)
-      attn_dma<D, VB, true>(a, wbuf + k * C::STAGE, row0 + cb, t_end - cb, lane);
+      attn_dma<D, KB, VB, true>(a, wbuf + k * C::STAGE, row0 + cb, t_end - cb, lane);
   }
 
   // ---- query row n of the tile: query jr / rep, head jr % rep of this kv head
@@ -1021,7 +1067,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = (i & 1) ? bf16_hi(ws[i >> 1]) : bf16_lo(ws[i >> 1]);
+      const int e = key_elem8<KB>(i);  // the key operand's element at byte i
+      const float x = (e & 1) ? bf16_hi(ws[e >> 1]) : bf16_lo(ws[e >> 1]);
       const int v = (int)__builtin_rintf(x * qn);
       const int lo = ((v + 128) & 255) - 128;
       const int hi = (v - lo) >> 8;
@@ -1062,9 +1109,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int cbn = cb + 4 * CH * (S - 1);
     const int nslot = slot == 0 ? S - 1 : slot - 1;
     if (cbn + CH <= t_end)
-      attn_dma<D, VB, false>(a, wbuf + nslot * C::STAGE, row0 + cbn, CH, lane);
+      attn_dma<D, KB, VB, false>(a, wbuf + nslot * C::STAGE, row0 + cbn, CH, lane);
     else if (cbn < t_end)
-      attn_dma<D, VB, true>(a, wbuf + nslot * C::STAGE, row0 + cbn, t_end - cbn, lane);
+      attn_dma<D, KB, VB, true>(a, wbuf + nslot * C::STAGE, row0 + cbn, t_end - cbn, lane);
     const int later = (t_end - cb - 1) / (4 * CH);
     if (later >= 2 && S == 3)
       wait_vmcnt<(S - 1) * C::NI>();
@@ -1078,7 +1125,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int tl = t_end - cb;
     const bool full = tl >= CH;
 
-    stage_value_scales<D, VB>(sp, full, tl, lane, E, acc,
+    stage_value_scales<D, KB, VB>(sp, full, tl, lane, E, acc,
                               [](int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); });
 
     // ---- scores: lane (c, n) gets row n at tokens 16 tau + 4c + i
@@ -1092,9 +1139,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       float T[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int ch = 2 * g + (c >> 1);
-        const long kw = *(const __attribute__((address_space(3))) long*)(
-            sp + 16 * (tk * C::CPR + (ch ^ (tk & (C::SW - 1)))) + 8 * (c & 1));
+        // this lane's 8 key indices: elements 32 g + 8 c .. + 7 of token tk
+        constexpr int BO = 8 * KB / 8;
+        const int bo = (4 * g + c) * BO, ch = bo >> 4;
+        const long kw = keys8<KB>(sp + 16 * (tk * C::CPR + (ch ^ (tk & (C::SW - 1)))) + (bo & 15));
         const tq_i32x4 dh = __builtin_amdgcn_mfma_i32_16x16x32_i8(kw, qh[g], zero4, 0, 0, 0);
         const tq_i32x4 dl = __builtin_amdgcn_mfma_i32_16x16x32_i8(kw, ql[g], zero4, 0, 0, 0);
 #pragma unroll
@@ -1381,7 +1429,11 @@ static void launch_combine(const AttnArgs& a, hipStream_t st) {
   }
 }
 
-bool decode_attn_uses_mfma(int d, int kb, int vb) { return d <= 256 && kb == 8 && vb <= 5; }
+// int8 keys, and packed 4- and 2-bit keys spread into bytes (2-bit rows of
+// d = 64 are too short for the 16-byte copies); values of 2 to 5 bits
+bool decode_attn_uses_mfma(int d, int kb, int vb) {
+  return d <= 256 && vb <= 5 && (kb == 8 || kb == 4 || (kb == 2 && d >= 128));
+}
 
 void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n_q_heads, int n_kv_heads,
                           int max_ctx, int* splits, int* tokens_per_split) {
@@ -1392,7 +1444,7 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   const long long rep = n_q_heads / n_kv_heads, nrow = (long long)n_queries * rep;
   // query rows per block: 16 on the matrix-core path once a kv head has more
   // than one tile of four
-  const long long rows = mfma && nrow > kHeadTile ? 16 : kHeadTile;
+  const long long rows = mfma && kb != 2 && nrow > kHeadTile ? 16 : kHeadTile;
   long long units = (long long)batch * n_kv_heads * ((nrow + rows - 1) / rows);
   if (units < 1) units = 1;  // an empty batch: nothing runs, any split count serves
   // The matrix-core kernel streams through per-wave DMA stages, which pay a
@@ -1437,6 +1489,30 @@ static void launch_split_kb(const AttnArgs& a, int vb, dim3 grid, hipStream_t st
   }
 }
 
+// Matrix-core launches: 16 (query, head) rows per block once a kv head has
+// more than four (not for 2-bit keys, which take the four-row kernel's tiles).
+template <int D, int KB>
+static void launch_mfma_kb(const AttnArgs& w, int vb, int nrow, dim3 grid, hipStream_t st) {
+  if constexpr (KB != 2) {
+    if (nrow > kHeadTile) {
+      const dim3 g16((unsigned)(w.batch * w.n_kv_heads * ((nrow + 15) / 16) * w.splits));
+      switch (vb) {
+        case 2: decode_attn_mfma16_kernel<D, KB, 2><<<g16, 256, 0, st>>>(w); break;
+        case 3: decode_attn_mfma16_kernel<D, KB, 3><<<g16, 256, 0, st>>>(w); break;
+        case 4: decode_attn_mfma16_kernel<D, KB, 4><<<g16, 256, 0, st>>>(w); break;
+        default: decode_attn_mfma16_kernel<D, KB, 5><<<g16, 256, 0, st>>>(w); break;
+      }
+      return;
+    }
+  }
+  switch (vb) {
+    case 2: decode_attn_mfma_kernel<D, KB, 2><<<grid, 256, 0, st>>>(w); break;
+    case 3: decode_attn_mfma_kernel<D, KB, 3><<<grid, 256, 0, st>>>(w); break;
+    case 4: decode_attn_mfma_kernel<D, KB, 4><<<grid, 256, 0, st>>>(w); break;
+    default: decode_attn_mfma_kernel<D, KB, 5><<<grid, 256, 0, st>>>(w); break;
+  }
+}
+
 template <int D>
 static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t st) {
   const int rep = a.n_q_heads / a.n_kv_heads;
@@ -1452,22 +1528,12 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
       w.wide = ((uintptr_t)a.v_q & 15u) == 0 && ((uintptr_t)a.k_scale & 15u) == 0 &&
                ((uintptr_t)a.k_zero & 15u) == 0 && (a.seq_stride & 1) == 0 && (a.head_stride & 1) == 0;
       const int nrow = a.n_queries * rep;
-      if (nrow > kHeadTile) {
-        // 16 (query, head) rows per block
-        const dim3 g16((unsigned)(a.batch * a.n_kv_heads * ((nrow + 15) / 16) * a.splits));
-        switch (vb) {
-          case 2: decode_attn_mfma16_kernel<D, 2><<<g16, 256, 0, st>>>(w); break;
-          case 3: decode_attn_mfma16_kernel<D, 3><<<g16, 256, 0, st>>>(w); break;
-          case 4: decode_attn_mfma16_kernel<D, 4><<<g16, 256, 0, st>>>(w); break;
-          default: decode_attn_mfma16_kernel<D, 5><<<g16, 256, 0, st>>>(w); break;
-        }
-      } else {
-        switch (vb) {
-          case 2: decode_attn_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(w); break;
-          case 3: decode_attn_mfma_kernel<D, 3><<<grid, 256, 0, st>>>(w); break;
-          case 4: decode_attn_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(w); break;
-          default: decode_attn_mfma_kernel<D, 5><<<grid, 256, 0, st>>>(w); break;
-        }
+      switch (kb) {
+        case 2:
+          if constexpr (D >= 128) launch_mfma_kb<D, 2>(w, vb, nrow, grid, st);
+          break;
+        case 4: launch_mfma_kb<D, 4>(w, vb, nrow, grid, st); break;
+        default: launch_mfma_kb<D, 8>(w, vb, nrow, grid, st); break;
       }
       launch_combine<D>(a, st);
       return hipGetLastError();
