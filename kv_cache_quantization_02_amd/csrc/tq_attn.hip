@@ -337,10 +337,12 @@ template <int D, int KB, int VB>
 struct MfmaCfg {
   static constexpr int G = D / kGroup, GW = G / 2, NSET = (G + 3) / 4, NT = D / 16, CH = 32;
   static constexpr int KRB = KB == 8 ? D : D * KB / 8;       // key row bytes
-  static constexpr int CPR = KRB / 16, SW = CPR < 8 ? CPR : 8;  // key chunks per row, swizzle span
+  // key chunks per row, and the span of their XOR swizzle (none for the
+  // 5-chunk rows of 5-bit keys, which are read as unaligned fields)
+  static constexpr int CPR = KRB / 16, SW = (CPR & (CPR - 1)) ? 1 : (CPR < 8 ? CPR : 8);
   static constexpr int W = D * VB / 32;                      // packed value dwords per row
   static constexpr int RB = 4 * W;                           // packed value bytes per row
-  static constexpr int NK = CH * KRB / 1024;                 // 16-byte DMAs of key rows
+  static constexpr int NK = (CH * KRB + 1023) / 1024;        // 16-byte DMAs of key rows
   static constexpr int NV = CH * W / 64;                     // 4-byte DMAs of value rows
   static constexpr int SC_DW = CH * GW, NSP = (SC_DW + 63) / 64;  // per fp16 plane
   static constexpr int NI_TAIL = NK + NV + 3 * NSP;          // DMA instructions of a partial step
@@ -352,7 +354,7 @@ struct MfmaCfg {
   static constexpr int NVW = (CH * RB + 1023) / 1024;        // 16-byte DMAs of values (+ key planes)
   static constexpr int NI_FULL = WIDE ? NK + NVW + NSP : NI_TAIL;
   static constexpr int NI = NI_FULL < NI_TAIL ? NI_FULL : NI_TAIL;  // fewest per step (the waits count these)
-  static constexpr int OFF_V = CH * KRB;
+  static constexpr int OFF_V = NK * 1024;  // key rows (5-bit keys: padded to whole copies)
   static constexpr int OFF_KS = OFF_V + CH * RB;
   static constexpr int OFF_KZ = OFF_KS + NSP * 256;
   static constexpr int OFF_VS = OFF_KZ + NSP * 256;
@@ -367,7 +369,7 @@ struct MfmaCfg {
   static constexpr int S = (4 * 3 * STAGE + EXTRA <= 81920 && 2 * NI_TAIL <= 63) ? 3 : 2;
   static constexpr int ACC_BYTES = 4 * NT * 4 * 64 * 4;
   static constexpr int BUF = (4 * S * STAGE > ACC_BYTES) ? 4 * S * STAGE : ACC_BYTES;
-  static_assert(G % 2 == 0 && (CH * W) % 64 == 0 && (CH * KRB) % 1024 == 0, "step layout");
+  static_assert(G % 2 == 0 && (CH * W) % 64 == 0 && KRB % 16 == 0, "step layout");
   static_assert((S - 1) * NI_TAIL <= 63, "vmcnt range");
 };
 
@@ -399,7 +401,7 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t
 // KB * e of its words.
 template <int KB>
 constexpr int key_elem16(int i) {
-  return KB == 8 ? i : KB == 4 ? ((i >> 3) << 3) + 2 * (i & 3) + ((i >> 2) & 1) : 4 * (i & 3) + (i >> 2);
+  return (KB == 8 || KB == 5) ? i : KB == 4 ? ((i >> 3) << 3) + 2 * (i & 3) + ((i >> 2) & 1) : 4 * (i & 3) + (i >> 2);
 }
 template <int KB>
 constexpr int key_elem8(int i) {
@@ -421,6 +423,31 @@ __device__ __forceinline__ tq_i32x4 keys16(const lds_u8* p) {
     return tq_i32x4{(int)(w & m), (int)((w >> 2) & m), (int)((w >> 4) & m), (int)((w >> 6) & m)};
   }
 }
+// 16 five-bit indices: the 10 bytes at byte bo of a key row (bo even).  The
+// operand's dword k holds elements 4k .. 4k + 3 in its bytes.
+__device__ __forceinline__ tq_i32x4 keys16_5(const lds_u8* row, int bo) {
+  const lds_u32* w = (const lds_u32*)(row + (bo & ~3));
+  const uint32_t sh = (uint32_t)(bo & 3) * 8u;  // 0 or 16
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+  const uint32_t x = __builtin_amdgcn_alignbit(w1, w0, sh);  // field bits 0 .. 31
+  const uint32_t y = __builtin_amdgcn_alignbit(w2, w1, sh);  // 32 .. 63
+  const uint32_t z = w2 >> sh;                                // 64 .. 79 (low half)
+  uint32_t e[16];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) e[j] = (x >> (5 * j)) & 31u;
+  e[6] = __builtin_amdgcn_alignbit(y, x, 30) & 31u;
+#pragma unroll
+  for (int j = 7; j < 12; ++j) e[j] = (y >> (5 * j - 32)) & 31u;
+  e[12] = __builtin_amdgcn_alignbit(z, y, 28) & 31u;
+#pragma unroll
+  for (int j = 13; j < 16; ++j) e[j] = (z >> (5 * j - 64)) & 31u;
+  tq_i32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = (int)(e[4 * k] | (e[4 * k + 1] << 8) | (e[4 * k + 2] << 16) | (e[4 * k + 3] << 24));
+  return r;
+}
+
 // 8 indices from the bytes at p (8 or 4 of them)
 template <int KB>
 __device__ __forceinline__ long keys8(const lds_u8* p) {
@@ -441,7 +468,8 @@ __device__ __forceinline__ void attn_dma(const AttnArgs& a, lds_u8* stage, int64
   const uint8_t* kb = a.k_q + r0 * C::KRB;
 #pragma unroll
   for (int j = 0; j < C::NK; ++j) {
-    const int s = 64 * j + lane;
+    // lanes past the step's key chunks (5-bit keys) re-read the last one into the padding
+    const int s = min(64 * j + lane, C::CH * C::CPR - 1);
     int t = s / C::CPR;
     const int ch = (s % C::CPR) ^ (t & (C::SW - 1));
     if (TAIL) t = min(t, tl - 1);
@@ -797,7 +825,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             // this lane's 16 key indices: elements 64 gp + 16 c .. + 15 of the row
             constexpr int BO = 16 * KB / 8;  // their packed bytes
             const int bo = (4 * gp + c) * BO, ch = bo >> 4;
-            const tq_i32x4 kw = keys16<KB>(sp + 16 * (t * C::CPR + (ch ^ (t & (C::SW - 1)))) + (bo & 15));
+            tq_i32x4 kw;
+            if constexpr (KB == 5)
+              kw = keys16_5(sp + t * C::KRB, bo);
+            else
+              kw = keys16<KB>(sp + 16 * (t * C::CPR + (ch ^ (t & (C::SW - 1)))) + (bo & 15));
             dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(aqh[gp], kw, dh, 0, 0, 0);
             dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(aql[gp], kw, dl, 0, 0, 0);
           }
@@ -1429,10 +1461,11 @@ static void launch_combine(const AttnArgs& a, hipStream_t st) {
   }
 }
 
-// int8 keys, and packed 4- and 2-bit keys spread into bytes (2-bit rows of
-// d = 64 are too short for the 16-byte copies); values of 2 to 5 bits
+// int8 keys, and packed 5-, 4- and 2-bit keys spread into bytes (2- and
+// 5-bit rows of d = 64 do not keep the 16-byte alignment of the copies);
+// values of 2 to 5 bits
 bool decode_attn_uses_mfma(int d, int kb, int vb) {
-  return d <= 256 && vb <= 5 && (kb == 8 || kb == 4 || (kb == 2 && d >= 128));
+  return d <= 256 && vb <= 5 && (kb == 8 || kb == 4 || ((kb == 2 || kb == 5) && d >= 128));
 }
 
 void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n_q_heads, int n_kv_heads,
@@ -1444,7 +1477,7 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   const long long rep = n_q_heads / n_kv_heads, nrow = (long long)n_queries * rep;
   // query rows per block: 16 on the matrix-core path once a kv head has more
   // than one tile of four
-  const long long rows = mfma && kb != 2 && nrow > kHeadTile ? 16 : kHeadTile;
+  const long long rows = mfma && (kb == 8 || kb == 4) && nrow > kHeadTile ? 16 : kHeadTile;
   long long units = (long long)batch * n_kv_heads * ((nrow + rows - 1) / rows);
   if (units < 1) units = 1;  // an empty batch: nothing runs, any split count serves
   // The matrix-core kernel streams through per-wave DMA stages, which pay a
@@ -1490,10 +1523,11 @@ static void launch_split_kb(const AttnArgs& a, int vb, dim3 grid, hipStream_t st
 }
 
 // Matrix-core launches: 16 (query, head) rows per block once a kv head has
-// more than four (not for 2-bit keys, which take the four-row kernel's tiles).
+// more than four (8- and 4-bit keys; 2- and 5-bit keys take the four-row
+// kernel's tiles).
 template <int D, int KB>
 static void launch_mfma_kb(const AttnArgs& w, int vb, int nrow, dim3 grid, hipStream_t st) {
-  if constexpr (KB != 2) {
+  if constexpr (KB == 8 || KB == 4) {
     if (nrow > kHeadTile) {
       const dim3 g16((unsigned)(w.batch * w.n_kv_heads * ((nrow + 15) / 16) * w.splits));
       switch (vb) {
@@ -1533,6 +1567,9 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
           if constexpr (D >= 128) launch_mfma_kb<D, 2>(w, vb, nrow, grid, st);
           break;
         case 4: launch_mfma_kb<D, 4>(w, vb, nrow, grid, st); break;
+        case 5:
+          if constexpr (D >= 128) launch_mfma_kb<D, 5>(w, vb, nrow, grid, st);
+          break;
         default: launch_mfma_kb<D, 8>(w, vb, nrow, grid, st); break;
       }
       launch_combine<D>(a, st);

@@ -218,10 +218,10 @@ def test_sixteen_row_tiles(B, M, Hq, Hkv, N, d, vb, ctx):
                 assert not got[b, m].any()
 
 
-# Packed 4- and 2-bit keys run on the matrix cores too: their indices are
-# spread into bytes and the query operand follows their order.  One query
-# (four rows), 16-row tiles (4-bit keys) and 2-bit keys over several rows
-# (four-row tiles).
+# Packed 5-, 4- and 2-bit keys run on the matrix cores too: their indices
+# are spread into bytes and the query operand follows their order.  One
+# query (four rows), 16-row tiles (4-bit keys), and 2- and 5-bit keys over
+# several rows (four-row tiles).
 @pytest.mark.parametrize("B,M,Hq,Hkv,N,d,kb,vb,ctx", [
     (2, 1, 8, 2, 300, 128, 4, 3, [300, 171]),
     (2, 1, 8, 2, 300, 128, 2, 2, [300, 33]),
@@ -230,6 +230,9 @@ def test_sixteen_row_tiles(B, M, Hq, Hkv, N, d, vb, ctx):
     (1, 9, 8, 4, 700, 64, 4, 2, [700]),
     (2, 4, 16, 4, 400, 128, 2, 3, [400, 3]),
     (1, 1, 32, 8, 9000, 256, 2, 4, [9000]),
+    (2, 1, 8, 2, 300, 128, 5, 3, [300, 171]),
+    (2, 4, 16, 4, 400, 256, 5, 2, [400, 97]),
+    (1, 1, 32, 8, 9000, 128, 5, 5, [9000]),
 ])
 def test_packed_keys_on_matrix_cores(B, M, Hq, Hkv, N, d, kb, vb, ctx):
     got, ref = run_mq_case(B, M, Hq, Hkv, N, d, kb, vb, ctx, 26, f"packed keys k{kb}v{vb} d{d} M{M} rep{Hq // Hkv}")
@@ -239,7 +242,7 @@ def test_packed_keys_on_matrix_cores(B, M, Hq, Hkv, N, d, kb, vb, ctx):
                 assert not got[b, m].any()
 
 
-@pytest.mark.parametrize("kb", [4, 2])
+@pytest.mark.parametrize("kb", [5, 4, 2])
 @pytest.mark.parametrize("k_mul,v_mul,q_mul", [(1e-5, 1.0, 2e5), (1.0, 1.0, 1e-3), (1e3, 300.0, 1e-3)])
 def test_packed_key_magnitudes(kb, k_mul, v_mul, q_mul):
     run_mq_case(2, 4, 16, 4, 400, 128, kb, 3, [400, 233], 27, f"packed k{kb} k*{k_mul} v*{v_mul} q*{q_mul}",
