@@ -344,8 +344,11 @@ struct MfmaCfg {
   static constexpr int RB = 4 * W;                           // packed value bytes per row
   static constexpr int NK = (CH * KRB + 1023) / 1024;        // 16-byte DMAs of key rows
   static constexpr int NV = CH * W / 64;                     // 4-byte DMAs of value rows
+  // value rows that fill whole 16-byte copies go 16 bytes per lane in every step
+  static constexpr bool VX4 = (CH * RB) % 1024 == 0;
+  static constexpr int NVX = CH * RB / 1024;
   static constexpr int SC_DW = CH * GW, NSP = (SC_DW + 63) / 64;  // per fp16 plane
-  static constexpr int NI_TAIL = NK + NV + 3 * NSP;          // DMA instructions of a partial step
+  static constexpr int NI_TAIL = NK + (VX4 ? NVX : NV) + 3 * NSP;  // DMA instructions of a partial step
   // A full step can copy its value rows 16 bytes per lane.  When they leave
   // half an instruction over and the key scale and zero planes of the step
   // fill exactly that half (d = 128: 2 x 256 bytes), the last instruction's
@@ -360,8 +363,11 @@ struct MfmaCfg {
   static constexpr int OFF_VS = OFF_KZ + NSP * 256;
   static constexpr int STAGE = OFF_VS + NSP * 256;
   static constexpr int PB = 4 * CH;   // p[head][slot], then 32 zeros
-  static constexpr int LUT = 1 << (2 * VB);
-  static constexpr int OFF_PB = LUT * 4 > 256 ? LUT * 4 : 256;
+  // centroid table: fp16 pairs for two indices of up to 5 bits, single fp16
+  // entries for 8-bit indices
+  static constexpr int LUT = VB == 8 ? 256 : 1 << (2 * VB);
+  static constexpr int LUT_BYTES = VB == 8 ? 2 * LUT : 4 * LUT;
+  static constexpr int OFF_PB = LUT_BYTES > 256 ? LUT_BYTES : 256;
   static constexpr int OFF_STATS = OFF_PB + 4 * (PB + 32) * 4;
   static constexpr int OFF_BUF = OFF_STATS + 4 * 4 * 2 * 4;
   static constexpr int EXTRA = OFF_BUF + 1024;
@@ -460,6 +466,59 @@ __device__ __forceinline__ long keys8(const lds_u8* p) {
   }
 }
 
+// The block's centroid table in LDS: for value widths up to 5 bits the fp16
+// pair (centroid[i & (2^VB - 1)], centroid[i >> VB]) at word i, so that one
+// lookup of two adjacent indices yields both; for 8-bit values the fp16
+// centroid[i] at half-word i.
+template <int VB>
+__device__ __forceinline__ void fill_centroid_lut(uint8_t* lds) {
+  const uint32_t* cen = attn_centroids<VB>();
+  if constexpr (VB == 8) {
+    uint16_t* t = reinterpret_cast<uint16_t*>(lds);
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) t[i] = (uint16_t)half2_bits(__uint_as_float(cen[i]), 0.f);
+  } else {
+    uint32_t* t = reinterpret_cast<uint32_t*>(lds);
+    for (int i = threadIdx.x; i < (1 << (2 * VB)); i += blockDim.x)
+      t[i] = half2_bits(__uint_as_float(cen[i & ((1 << VB) - 1)]), __uint_as_float(cen[i >> VB]));
+  }
+}
+
+// PV B operands of one group: the fp16 centroids at this lane's two dims for
+// the 8 tokens of its contraction slots (f[i]: the first value dword of
+// token i's group at the lane's field; fsh: the field's bit offset).  b0
+// feeds tile 2g (dim 2n), b1 tile 2g+1 (dim 2n+1).
+template <int VB, int LUT>
+__device__ __forceinline__ void centroid_operands(const lds_u32* const (&f)[8], uint32_t fsh, const lds_u8* lut,
+                                                  uint32_t (&b0)[4], uint32_t (&b1)[4]) {
+  if constexpr (VB == 8) {
+    // two byte indices side by side: one table read each
+    uint32_t L0[8], L1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t x = f[i][0] >> fsh;
+      L0[i] = *(const __attribute__((address_space(3))) uint16_t*)(lut + ((x << 1) & 0x1FEu));
+      L1[i] = *(const __attribute__((address_space(3))) uint16_t*)(lut + ((x >> 7) & 0x1FEu));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      b0[m] = __builtin_amdgcn_perm(L0[2 * m + 1], L0[2 * m], 0x05040100u);
+      b1[m] = __builtin_amdgcn_perm(L1[2 * m + 1], L1[2 * m], 0x05040100u);
+    }
+  } else {
+    uint32_t L[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t x = __builtin_amdgcn_alignbit(f[i][1], f[i][0], fsh);
+      L[i] = *(const lds_u32*)(lut + (x & ((uint32_t)(LUT - 1) << 2)));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      b0[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x05040100u);
+      b1[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x07060302u);
+    }
+  }
+}
+
 // Issue the DMAs of the step whose first row is r0 into `stage`.  TAIL: only
 // the first tl rows are inside the context; later rows re-read row tl - 1.
 template <int D, int KB, int VB, bool TAIL>
@@ -498,15 +557,28 @@ __device__ __forceinline__ void attn_dma(const AttnArgs& a, lds_u8* stage, int64
     return;
   }
   const uint8_t* vb = a.v_q + r0 * C::RB;
+  if constexpr (C::VX4) {
 #pragma unroll
-  for (int j = 0; j < C::NV; ++j) {
-    const int s = 64 * j + lane;
-    int off = 4 * s;
-    if (TAIL) {
-      const int t = s / C::W;
-      off = 4 * (min(t, tl - 1) * C::W + (s - t * C::W));
+    for (int j = 0; j < C::NVX; ++j) {
+      const int s = 64 * j + lane;
+      int off = 16 * s;
+      if (TAIL) {
+        const int t = off / C::RB;
+        off = min(t, tl - 1) * C::RB + (off - t * C::RB);
+      }
+      dma_x4(vb, (uint32_t)off, lds_addr(stage + C::OFF_V + 1024 * j));
     }
-    dma_x1(vb, (uint32_t)off, lds_addr(stage + C::OFF_V + 256 * j));
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::NV; ++j) {
+      const int s = 64 * j + lane;
+      int off = 4 * s;
+      if (TAIL) {
+        const int t = s / C::W;
+        off = 4 * (min(t, tl - 1) * C::W + (s - t * C::W));
+      }
+      dma_x1(vb, (uint32_t)off, lds_addr(stage + C::OFF_V + 256 * j));
+    }
   }
   const uint16_t* planes[3] = {a.k_scale, a.k_zero, a.v_scale};
 #pragma unroll
@@ -614,11 +686,10 @@ __device__ __forceinline__ void stage_value_scales(lds_u8* sp, bool full, int tl
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_attn_mfma_kernel(AttnArgs a) {
   using C = MfmaCfg<D, KB, VB>;
-  constexpr int G = C::G, GW = C::GW, NSET = C::NSET, NT = C::NT, CH = C::CH, W = C::W, S = C::S;
+  constexpr int G = C::G, NSET = C::NSET, NT = C::NT, CH = C::CH, W = C::W, S = C::S;
   // one LDS block: the centroid-pair table first (its byte offsets are the
   // masked index bits themselves), then p, the merge statistics, the stages
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[C::OFF_BUF + C::BUF];
-  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(lds_all);
   float(*const stats)[4][2] = reinterpret_cast<float(*)[4][2]>(lds_all + C::OFF_STATS);
   uint8_t* const smem = lds_all + C::OFF_BUF;
 
@@ -648,12 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   lds_f32* const pb = (lds_f32*)(lds_all + C::OFF_PB) + wave * (C::PB + 32);
   lds_u8* const lut = (lds_u8*)lds_all;
 
-  for (int i = threadIdx.x; i < C::LUT; i += blockDim.x) {
-    const uint32_t* cen = attn_centroids<VB>();
-    const float c0 = __uint_as_float(cen[i & ((1 << VB) - 1)]);
-    const float c1 = __uint_as_float(cen[i >> VB]);
-    lut_s[i] = half2_bits(c0, c1);
-  }
+  fill_centroid_lut<VB>(lds_all);
   if (lane < 32) pb[C::PB + lane] = 0.f;
 
   int ctx = a.ctx_lens[b];
@@ -763,11 +829,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // value fields: dims 32g + 2n, +1 sit at bits 2VB n of group g's segment;
   // read the dword pair whose funnel shift leaves them at bit 2
   int fk = (2 * VB * n) >> 5, fsh = (2 * VB * n) & 31;
-  if (fsh < 2) {
-    fk -= 1;
-    fsh += 30;
-  } else {
-    fsh -= 2;
+  if constexpr (VB != 8) {
+    // the pair's bits go to bit 2 of the table's byte offset
+    if (fsh < 2) {
+      fk -= 1;
+      fsh += 30;
+    } else {
+      fsh -= 2;
+    }
   }
   const int vdw = C::OFF_V / 4 + c * W + fk;  // + 4W i + VB g for token c + 4i, group g
   __syncthreads();
@@ -910,19 +979,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       uint32_t aw[4];
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) aw[k2] = pk_mul_f16(ph[k2], sv[k2][g]);
-      uint32_t L[8];
+      const lds_u32* f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const lds_u32* f = (i < 4 ? vrow0 : vrow1) + 4 * W * (i & 3) + VB * g;
-        const uint32_t x = __builtin_amdgcn_alignbit(f[1], f[0], (uint32_t)fsh);
-        L[i] = *(const lds_u32*)(lut + (x & ((uint32_t)(C::LUT - 1) << 2)));
-      }
+      for (int i = 0; i < 8; ++i) f[i] = (i < 4 ? vrow0 : vrow1) + 4 * W * (i & 3) + VB * g;
       uint32_t b0[4], b1[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        b0[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x05040100u);
-        b1[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x07060302u);
-      }
+      centroid_operands<VB, C::LUT>(f, (uint32_t)fsh, lut, b0, b1);
       const tq_half8 ap = __builtin_bit_cast(tq_half8, aw);
       acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(tq_half8, b0), acc[2 * g], 0, 0, 0);
       acc[2 * g + 1] =
@@ -1017,7 +1078,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   constexpr int G = C::G, NT = C::NT, CH = C::CH, W = C::W, S = C::S;
   constexpr int R = 16;  // query rows per block
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[C::OFF_BUF + C::BUF];
-  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(lds_all);
   // the other kernel's p buffers hold the row statistics here
   static_assert(C::OFF_STATS - C::OFF_PB >= 4 * R * 2 * 4, "row statistics fit");
   float(*const stats)[R][2] = reinterpret_cast<float(*)[R][2]>(lds_all + C::OFF_PB);
@@ -1044,10 +1104,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   lds_u8* const wbuf = (lds_u8*)smem + wave * S * C::STAGE;
   lds_u8* const lut = (lds_u8*)lds_all;
 
-  for (int i = threadIdx.x; i < C::LUT; i += blockDim.x) {
-    const uint32_t* cen = attn_centroids<VB>();
-    lut_s[i] = half2_bits(__uint_as_float(cen[i & ((1 << VB) - 1)]), __uint_as_float(cen[i >> VB]));
-  }
+  fill_centroid_lut<VB>(lds_all);
 
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
@@ -1118,11 +1175,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // value fields: as in the kernel above; contraction slot 8c + i is token
   // 4c + i (i < 4) or 16 + 4c + (i - 4)
   int fk = (2 * VB * n) >> 5, fsh = (2 * VB * n) & 31;
-  if (fsh < 2) {
-    fk -= 1;
-    fsh += 30;
-  } else {
-    fsh -= 2;
+  if constexpr (VB != 8) {
+    // the pair's bits go to bit 2 of the table's byte offset
+    if (fsh < 2) {
+      fk -= 1;
+      fsh += 30;
+    } else {
+      fsh -= 2;
+    }
   }
   const int vdw = C::OFF_V / 4 + 4 * c * W + fk;
   __syncthreads();
@@ -1238,19 +1298,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       uint32_t aw[4];
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) aw[k2] = pk_mul_f16(ph[k2], sv[k2][g]);
-      uint32_t L[8];
+      const lds_u32* f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const lds_u32* f = (i < 4 ? vrow0 : vrow1) + W * (i & 3) + VB * g;
-        const uint32_t x = __builtin_amdgcn_alignbit(f[1], f[0], (uint32_t)fsh);
-        L[i] = *(const lds_u32*)(lut + (x & ((uint32_t)(C::LUT - 1) << 2)));
-      }
+      for (int i = 0; i < 8; ++i) f[i] = (i < 4 ? vrow0 : vrow1) + W * (i & 3) + VB * g;
       uint32_t b0[4], b1[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        b0[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x05040100u);
-        b1[m] = __builtin_amdgcn_perm(L[2 * m + 1], L[2 * m], 0x07060302u);
-      }
+      centroid_operands<VB, C::LUT>(f, (uint32_t)fsh, lut, b0, b1);
       const tq_half8 ap = __builtin_bit_cast(tq_half8, aw);
       acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(tq_half8, b0), acc[2 * g], 0, 0, 0);
       acc[2 * g + 1] =
@@ -1465,7 +1517,7 @@ static void launch_combine(const AttnArgs& a, hipStream_t st) {
 // 5-bit rows of d = 64 do not keep the 16-byte alignment of the copies);
 // values of 2 to 5 bits
 bool decode_attn_uses_mfma(int d, int kb, int vb) {
-  return d <= 256 && vb <= 5 && (kb == 8 || kb == 4 || ((kb == 2 || kb == 5) && d >= 128));
+  return d <= 256 && (vb <= 5 || vb == 8) && (kb == 8 || kb == 4 || ((kb == 2 || kb == 5) && d >= 128));
 }
 
 void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n_q_heads, int n_kv_heads,
@@ -1534,7 +1586,8 @@ static void launch_mfma_kb(const AttnArgs& w, int vb, int nrow, dim3 grid, hipSt
         case 2: decode_attn_mfma16_kernel<D, KB, 2><<<g16, 256, 0, st>>>(w); break;
         case 3: decode_attn_mfma16_kernel<D, KB, 3><<<g16, 256, 0, st>>>(w); break;
         case 4: decode_attn_mfma16_kernel<D, KB, 4><<<g16, 256, 0, st>>>(w); break;
-        default: decode_attn_mfma16_kernel<D, KB, 5><<<g16, 256, 0, st>>>(w); break;
+        case 5: decode_attn_mfma16_kernel<D, KB, 5><<<g16, 256, 0, st>>>(w); break;
+        default: decode_attn_mfma16_kernel<D, KB, 8><<<g16, 256, 0, st>>>(w); break;
       }
       return;
     }
@@ -1543,7 +1596,8 @@ static void launch_mfma_kb(const AttnArgs& w, int vb, int nrow, dim3 grid, hipSt
     case 2: decode_attn_mfma_kernel<D, KB, 2><<<grid, 256, 0, st>>>(w); break;
     case 3: decode_attn_mfma_kernel<D, KB, 3><<<grid, 256, 0, st>>>(w); break;
     case 4: decode_attn_mfma_kernel<D, KB, 4><<<grid, 256, 0, st>>>(w); break;
-    default: decode_attn_mfma_kernel<D, KB, 5><<<grid, 256, 0, st>>>(w); break;
+    case 5: decode_attn_mfma_kernel<D, KB, 5><<<grid, 256, 0, st>>>(w); break;
+    default: decode_attn_mfma_kernel<D, KB, 8><<<grid, 256, 0, st>>>(w); break;
   }
 }
 

@@ -221,7 +221,9 @@ def test_sixteen_row_tiles(B, M, Hq, Hkv, N, d, vb, ctx):
 # Packed 5-, 4- and 2-bit keys run on the matrix cores too: their indices
 # are spread into bytes and the query operand follows their order.  One
 # query (four rows), 16-row tiles (4-bit keys), and 2- and 5-bit keys over
-# several rows (four-row tiles).
+# several rows (four-row tiles).  8-bit values take single-entry centroid
+# lookups; value rows that fill whole 16-byte copies (v8, v4, v2 at d >= 128)
+# are copied 16 bytes per lane.
 @pytest.mark.parametrize("B,M,Hq,Hkv,N,d,kb,vb,ctx", [
     (2, 1, 8, 2, 300, 128, 4, 3, [300, 171]),
     (2, 1, 8, 2, 300, 128, 2, 2, [300, 33]),
@@ -233,6 +235,12 @@ def test_sixteen_row_tiles(B, M, Hq, Hkv, N, d, vb, ctx):
     (2, 1, 8, 2, 300, 128, 5, 3, [300, 171]),
     (2, 4, 16, 4, 400, 256, 5, 2, [400, 97]),
     (1, 1, 32, 8, 9000, 128, 5, 5, [9000]),
+    (2, 1, 8, 2, 300, 128, 8, 8, [300, 171]),
+    (2, 4, 16, 4, 520, 128, 8, 8, [520, 250]),
+    (2, 1, 12, 2, 400, 256, 8, 8, [400, 257]),
+    (2, 2, 8, 2, 300, 64, 4, 8, [300, 77]),
+    (1, 1, 32, 8, 9000, 128, 8, 4, [9000]),
+    (2, 3, 8, 2, 300, 256, 8, 2, [300, 200]),
 ])
 def test_packed_keys_on_matrix_cores(B, M, Hq, Hkv, N, d, kb, vb, ctx):
     got, ref = run_mq_case(B, M, Hq, Hkv, N, d, kb, vb, ctx, 26, f"packed keys k{kb}v{vb} d{d} M{M} rep{Hq // Hkv}")
