@@ -1356,6 +1356,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   }
 }
 
+// Merge the partials of splits s0, s0 + ds, ... (NB of them, those below
+// `splits`) into the running (mm, ll, acc) of one row slice: all their
+// loads issue before the first is used, the batch maximum rescales the
+// running sums once, then the batch adds in split order.
+template <int D, int NB>
+__device__ __forceinline__ void merge_batch(const float* part, int s0, int ds, int splits, int sub, float& mm,
+                                            float& ll, float (&acc)[8]) {
+  float ms[NB], ls[NB];
+  float4 x0[NB], x1[NB];
+  // splits past the last re-read the last one (no branch between the loads,
+  // so they are all in flight together) and count as empty
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int s = min(s0 + j * ds, splits - 1);
+    const float* ps = part + s * part_stride<D>();
+    const float2 ml = *reinterpret_cast<const float2*>(ps + D);
+    ms[j] = ml.x;
+    ls[j] = ml.y;
+    x0[j] = *reinterpret_cast<const float4*>(ps + 8 * sub);
+    x1[j] = *reinterpret_cast<const float4*>(ps + 8 * sub + 4);
+  }
+  // keep every load above this point (the scheduler would otherwise trade
+  // the overlap for registers, one round trip per split)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    if (s0 + j * ds >= splits) ms[j] = -INFINITY;
+  float mb = mm;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) mb = fmaxf(mb, ms[j]);
+  // A split with no tokens carries m = -inf and adds nothing.  No branch on
+  // it either, which would let the compiler hold back the partials' loads:
+  // with everything so far empty the reference maximum is 0 and every
+  // weight exp2(-inf) = 0.
+  const float mref = (mb == -INFINITY) ? 0.f : mb;
+  const float c = exp2f(mm - mref);  // 0 while nothing is merged yet
+  ll *= c;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] *= c;
+  mm = mb;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const float f = exp2f(ms[j] - mref);
+    ll += ls[j] * f;
+    acc[0] += x0[j].x * f; acc[1] += x0[j].y * f; acc[2] += x0[j].z * f; acc[3] += x0[j].w * f;
+    acc[4] += x1[j].x * f; acc[5] += x1[j].y * f; acc[6] += x1[j].z * f; acc[7] += x1[j].w * f;
+  }
+}
+
+// Splits first, first + ds, ... below `splits` merged in batches sized to
+// their count (the count is uniform over the grid; loads for splits that do
+// not exist are wasted issue slots).
+template <int D>
+__device__ __forceinline__ void merge_splits(const float* part, int sub, int first, int ds, int splits, float& mm,
+                                             float& ll, float (&acc)[8]) {
+  const int n = (splits + ds - 1) / ds;
+  if (n <= 1) {
+    merge_batch<D, 1>(part, first, ds, splits, sub, mm, ll, acc);
+  } else if (n <= 2) {
+    merge_batch<D, 2>(part, first, ds, splits, sub, mm, ll, acc);
+  } else if (n <= 4) {
+    merge_batch<D, 4>(part, first, ds, splits, sub, mm, ll, acc);
+  } else {
+    for (int s0 = first; s0 < splits; s0 += 8 * ds) merge_batch<D, 8>(part, s0, ds, splits, sub, mm, ll, acc);
+  }
+}
+
 // Merge the splits of each (sequence, query head), un-rotate once, store bf16.
 template <int D>
 __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
@@ -1366,48 +1433,12 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
   const bool active = r0 < rows;
   const int r = active ? r0 : 0;
   const float* part = a.part + (int64_t)r * a.splits * part_stride<D>();
-  // splits are read SB at a time so that their loads are in flight together;
-  // the merge itself runs in split order
-  constexpr int SB = 8;
-  float mm = -INFINITY;
-  for (int s0 = 0; s0 < a.splits; s0 += SB) {
-    float mv[SB];
-#pragma unroll
-    for (int j = 0; j < SB; ++j) mv[j] = (s0 + j < a.splits) ? part[(s0 + j) * part_stride<D>() + D] : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < SB; ++j) mm = fmaxf(mm, mv[j]);
-  }
-  float ll = 0.f, acc[8];
+  // one pass over the splits, SB at a time so that their loads are in
+  // flight together; the running maximum rescales what is merged so far
+  float mm = -INFINITY, ll = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (mm != -INFINITY) {
-    for (int s0 = 0; s0 < a.splits; s0 += SB) {
-      float ms[SB], ls[SB];
-      float4 x0[SB], x1[SB];
-#pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        if (s0 + j < a.splits) {
-          const float* ps = part + (s0 + j) * part_stride<D>();
-          ms[j] = ps[D];
-          ls[j] = ps[D + 1];
-          x0[j] = *reinterpret_cast<const float4*>(ps + 8 * sub);
-          x1[j] = *reinterpret_cast<const float4*>(ps + 8 * sub + 4);
-        } else {
-          ms[j] = -INFINITY;
-          ls[j] = 0.f;
-          x0[j] = x1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        if (s0 + j >= a.splits) break;
-        const float f = exp2f(ms[j] - mm);
-        ll += ls[j] * f;
-        acc[0] += x0[j].x * f; acc[1] += x0[j].y * f; acc[2] += x0[j].z * f; acc[3] += x0[j].w * f;
-        acc[4] += x1[j].x * f; acc[5] += x1[j].y * f; acc[6] += x1[j].z * f; acc[7] += x1[j].w * f;
-      }
-    }
-  }
+  merge_splits<D>(part, sub, 0, 1, a.splits, mm, ll, acc);
   const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] *= inv;
@@ -1441,22 +1472,10 @@ __global__ __launch_bounds__(256) void decode_attn_combine_wide_kernel(AttnArgs 
   const int sub = threadIdx.x % LPR, k = threadIdx.x / LPR;
   const int r = blockIdx.x;
   const float* part = a.part + (int64_t)r * a.splits * part_stride<D>();
-  float mm = -INFINITY;
-  for (int s = k; s < a.splits; s += NSL) mm = fmaxf(mm, part[s * part_stride<D>() + D]);
-  float ll = 0.f, acc[8];
+  float mm = -INFINITY, ll = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (mm != -INFINITY) {
-    for (int s = k; s < a.splits; s += NSL) {
-      const float* ps = part + s * part_stride<D>();
-      const float f = exp2f(ps[D] - mm);
-      ll += ps[D + 1] * f;
-      const float4 x0 = *reinterpret_cast<const float4*>(ps + 8 * sub);
-      const float4 x1 = *reinterpret_cast<const float4*>(ps + 8 * sub + 4);
-      acc[0] += x0.x * f; acc[1] += x0.y * f; acc[2] += x0.z * f; acc[3] += x0.w * f;
-      acc[4] += x1.x * f; acc[5] += x1.y * f; acc[6] += x1.z * f; acc[7] += x1.w * f;
-    }
-  }
+  merge_splits<D>(part, sub, k, NSL, a.splits, mm, ll, acc);
 #pragma unroll
   for (int i = 0; i < 8; ++i) s_acc[k][8 * sub + i] = acc[i];
   if (sub == 0) {

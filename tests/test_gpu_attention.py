@@ -283,6 +283,23 @@ def test_multi_query_matches_decode_at_m1():
     assert torch.equal(a.view(torch.int16), b.reshape(B, Hq, d).view(torch.int16))
 
 
+def _splits(sch, B, Hq, Hkv, N, d):
+    return tq.tq_decode_attn_workspace_bytes(sch, B, Hq, Hkv, N) // (B * Hq * (d + 4) * 4)
+
+
+# The merge reads each row's splits in batches sized to how many one lane
+# merges: one, two, four or eight at a time (the block-per-row merge spreads
+# 16 splits of d = 128 over a block), and eight at a time with a second
+# batch in the row-per-lanes merge of 9 to 15 splits.
+@pytest.mark.parametrize("Hq,Hkv,N,ctx,splits", [(32, 8, 2048, [2048], 16), (32, 8, 8192, [8192], 32),
+                                                 (16, 4, 8192, [8192], 64),
+                                                 (32, 8, 8192, [8192, 8000, 100, 4097, 1], 13)])
+def test_merge_batch_sizes(Hq, Hkv, N, ctx, splits):
+    d, kb, vb, B = 128, 8, 3, len(ctx)
+    assert _splits(tq.scheme(d, kb, vb), B, Hq, Hkv, N, d) == splits
+    run_case(B, Hq, Hkv, N, d, kb, vb, ctx, 29, f"merge of {splits} splits")
+
+
 @pytest.mark.parametrize("Hq,Hkv,N,d,kb,vb,ctx", [(4, 1, 9000, 128, 8, 3, [8999]), (12, 2, 9000, 256, 8, 3, [9000]),
                                                   (8, 2, 2600, 512, 5, 2, [2600]),
                                                   (4, 1, 9000, 128, 8, 3, [9000, 700]),
