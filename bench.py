@@ -136,6 +136,27 @@ def _time_us(fn, reps):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def _time_calls_us(fn, reps):
+    """(mean, median) microseconds of `reps` back-to-back calls after one
+    untimed pass, each call bracketed by its own pair of events.  `fn` is one
+    callable or a list of them, called in rotation (each on its own copy of
+    the data, so that rotating through copies larger than the 256 MB
+    last-level cache in total keeps every call reading HBM)."""
+    import torch
+    fns = fn if isinstance(fn, (list, tuple)) else [fn]
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    return sum(t) / reps, (t[(reps - 1) // 2] + t[reps // 2]) / 2
+
+
 def _time_rotating_us(fns, reps):
     """Mean microseconds per call of fns[i % len(fns)] over `reps` calls after one
     untimed pass over all of them (each fn works on its own copy of the data, so
@@ -191,8 +212,8 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     def fetch(rot):
         st = tq.tq_fetch_kv(sch, planes, B, Hkv, Hkv * N, N, N, lens, N, sig, rot, kw, vw)
         assert st == 0, st
-    us_e = _time_us(lambda: fetch(False), 10)
-    us_r = _time_us(lambda: fetch(True), 10)
+    us_e, med_e = _time_calls_us(lambda: fetch(False), 10)
+    us_r, med_r = _time_calls_us(lambda: fetch(True), 10)
     fb = B * Hkv * N * (row_bytes + 4 * d)
     # un-rotate the rotated V window back to the original domain (into the K buffer)
     rws = tq.contiguous_rows((B * Hkv * N, 1, 1))
@@ -200,7 +221,7 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     def unrot():
         st = tq.tq_unrotate_rows(d, vw, rws, sig, kw, rws)
         assert st == 0, st
-    us_u = _time_us(unrot, 10)
+    us_u, med_u = _time_calls_us(unrot, 10)
     del kw, vw, acache
     # growth of the decode cache by one 256-token step: every kept row read once,
     # the new storage written once
@@ -211,7 +232,7 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     def grow():
         st = tq.tq_grow_kv(sch, B, Hkv, planes, Hkv * N, N, N, gdst, Hkv * Ng, Ng, Ng)
         assert st == 0, st
-    us_g = _time_us(grow, 10)
+    us_g, med_g = _time_calls_us(grow, 10)
     gb = B * Hkv * (N + Ng) * row_bytes
     del gcache
     # multi-query (speculative, 4 query tokens per sequence) over the same cache
@@ -220,7 +241,7 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
     ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
     wsm = torch.empty(tq.tq_attn_quant_workspace_bytes(sch, B, M, 32, Hkv, N), dtype=torch.uint8, device=dev)
     om = torch.empty((B, M, 32, d), dtype=torch.bfloat16, device=dev)
-    us_m = _time_us(lambda: tq.attn_quant(qm, cache, ctx, sig, kb, vb, Hkv, out=om, workspace=wsm), 10)
+    us_m, med_m = _time_calls_us(lambda: tq.attn_quant(qm, cache, ctx, sig, kb, vb, Hkv, out=om, workspace=wsm), 10)
     # the pages' attention research shape: head_dim 256, GQA 6, one query, 16384 tokens
     s256 = tq.scheme(256, 8, 3)
     k6, v6 = synth.kv_inputs("normal", 1, 16384, 4, 256, 1007, device=dev)
@@ -243,17 +264,18 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
                       "us": us_a, "token_heads_per_s": rows / (us_a * 1e-6),
                       "GBps": rows * (4 * dd + tq.tq_row_bytes(tq.scheme(dd, akb, avb))) / (us_a * 1e-6) / 1e9},
         "fetch_kv_eager": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache",
-                           "us": us_e, "GBps": fb / (us_e * 1e-6) / 1e9},
+                           "us": us_e, "us_median": med_e, "GBps": fb / (us_e * 1e-6) / 1e9},
         "fetch_kv_rotated": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache, values rotated",
-                             "us": us_r, "GBps": fb / (us_r * 1e-6) / 1e9},
+                             "us": us_r, "us_median": med_r, "GBps": fb / (us_r * 1e-6) / 1e9},
         "grow_kv": {"workload": f"the {B}x{Hkv}x{N} k{kb}v{vb} cache re-laid at capacity {Ng} "
                                 f"(one 256-token growth step)",
-                    "us": us_g, "GBps": gb / (us_g * 1e-6) / 1e9, "algorithmic_bytes": gb},
+                    "us": us_g, "us_median": med_g, "GBps": gb / (us_g * 1e-6) / 1e9, "algorithmic_bytes": gb},
         "unrotate_rows": {"workload": f"{B * Hkv * N} bf16 rows of d={d} (the rotated V window)",
-                          "us": us_u, "GBps": B * Hkv * N * 4 * d / (us_u * 1e-6) / 1e9},
+                          "us": us_u, "us_median": med_u, "GBps": B * Hkv * N * 4 * d / (us_u * 1e-6) / 1e9},
         "attn_multi_query": {"workload": f"{M} causal queries per sequence over the {B}x{Hkv}x{N} k{kb}v{vb} cache, "
                                          f"32 query heads",
-                             "us": us_m, "cache_GBps": B * Hkv * N * row_bytes / (us_m * 1e-6) / 1e9},
+                             "us": us_m, "us_median": med_m,
+                             "cache_GBps": B * Hkv * N * row_bytes / (us_m * 1e-6) / 1e9},
         "attn_gqa6_d256": {"workload": "head_dim 256, GQA 6 (24 query / 4 kv heads), one query, 16384 tokens, k8v3; "
                                        "calls rotate over 40 copies of the 26 MB cache (HBM-resident)",
                            "us": us_6, "cache_GBps": b6 / (us_6 * 1e-6) / 1e9,
@@ -277,22 +299,26 @@ def measure_dense(tq, synth, k, v, dev):
     out = {}
     for tag, bits, qjl, gemms_q, gemms_dq in (("mse_b3", 3, False, 1, 2), ("qjl_b2+1", 2, True, 3, 3)):
         pj = proj if qjl else None
-        planes = tq.dense_quantize(x, rot, bits, pj)
+        # two plane buffers (436-470 MB each) in rotation, so that a
+        # dequantize does not find the planes it reads in the 256 MB
+        # last-level cache
+        copies = [tq.dense_quantize(x, rot, bits, pj) for _ in range(2)]
         back = torch.empty_like(x)
-        us_q = _time_us(lambda: tq.dense_quantize(x, rot, bits, pj, out=planes), 10)
-        us_d = _time_us(lambda: tq.dense_dequantize(planes, rot, bits, pj, out=back), 10)
+        us_q, med_q = _time_calls_us([lambda p=p: tq.dense_quantize(x, rot, bits, pj, out=p) for p in copies], 10)
+        us_d, med_d = _time_calls_us([lambda p=p: tq.dense_dequantize(p, rot, bits, pj, out=back) for p in copies],
+                                     10)
         sch = tq.dense_scheme(d, bits, qjl)
         pb = sum(max(tq.tq_dense_plane_row_bytes(sch, i), 0) for i in range(4))
-        for name, us, gemms in (("quantize", us_q, gemms_q), ("dequantize", us_d, gemms_dq)):
+        for name, us, med, gemms in (("quantize", us_q, med_q, gemms_q), ("dequantize", us_d, med_d, gemms_dq)):
             gbps = rows * (2 * d + pb) / (us * 1e-6) / 1e9
             tflops = rows * gemms * 2 * d * d / (us * 1e-6) / 1e12
             out[f"dense_{name}_{tag}"] = {
                 "workload": f"{rows} rows (prefill keys + values), d={d}, {tag}",
-                "kernel": f"dense_{name}_kernel<{d},{bits},{int(qjl)}>", "us": us,
+                "kernel": f"dense_{name}_kernel<{d},{bits},{int(qjl)}>", "us": us, "us_median": med,
                 "rows_per_s": rows / (us * 1e-6), "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBS,
                 "mfma_bf16_TFLOPs_executed": tflops, "frac_of_bf16_mfma_peak": tflops / 2500.0,
                 "plane_bytes_per_row": pb}
-        del planes, back
+        del copies, back
     del x
     return out
 
@@ -395,19 +421,27 @@ def measure_wide(tq, synth, dev):
         rec, L, T, H, d, kb, vb, seed = synth.WORKLOADS[wl]
         k, v = synth.kv_inputs(rec, L, T, H, d, seed, device=dev)
         sig = torch.from_numpy(synth.sign_vector(d)).to(dev)
-        planes = tq.alloc_planes(tq.scheme(d, kb, vb), (L, T, H), dev)
-        kout, vout = torch.empty_like(k), torch.empty_like(v)
-        us_q = _time_us(lambda: tq.quantize_kv(k, v, sig, kb, vb, out=planes), 10)
-        us_d = _time_us(lambda: tq.dequantize_kv(planes, sig, d, kb, vb, k_out=kout, v_out=vout), 10)
         rows = L * T * H
-        nbytes = rows * (4 * d + tq.tq_row_bytes(tq.scheme(d, kb, vb)))
-        for name, us in (("quantize", us_q), ("dequantize", us_d)):
+        plane_bytes = rows * tq.tq_row_bytes(tq.scheme(d, kb, vb))
+        # the planes (107-239 MB) would fit the 256 MB last-level cache: the
+        # calls rotate over copies totalling at least 768 MB, so that each
+        # dequantize reads planes from HBM as the prefill step's does
+        ncopy = max(2, -(-(768 << 20) // plane_bytes))
+        copies = [tq.alloc_planes(tq.scheme(d, kb, vb), (L, T, H), dev) for _ in range(ncopy)]
+        kout, vout = torch.empty_like(k), torch.empty_like(v)
+        us_q, med_q = _time_calls_us([lambda p=p: tq.quantize_kv(k, v, sig, kb, vb, out=p) for p in copies],
+                                     2 * ncopy + 6)
+        us_d, med_d = _time_calls_us([lambda p=p: tq.dequantize_kv(p, sig, d, kb, vb, k_out=kout, v_out=vout)
+                                      for p in copies], 2 * ncopy + 6)
+        nbytes = rows * 4 * d + plane_bytes
+        for name, us, med in (("quantize", us_q, med_q), ("dequantize", us_d, med_d)):
             gbps = nbytes / (us * 1e-6) / 1e9
-            out[f"{name}_{wl}"] = {"workload": f"{L}x{T}x{H} rows, d={d}, k{kb}v{vb}",
-                                   "kernel": f"{name}_kernel<{d},{kb},{vb}>", "us": us,
+            out[f"{name}_{wl}"] = {"workload": f"{L}x{T}x{H} rows, d={d}, k{kb}v{vb}; calls rotate over "
+                                               f"{ncopy} plane buffers",
+                                   "kernel": f"{name}_kernel<{d},{kb},{vb}>", "us": us, "us_median": med,
                                    "token_heads_per_s": rows / (us * 1e-6), "GBps": gbps,
                                    "frac_of_hbm_peak": gbps / HBM_PEAK_GBS}
-        del k, v, planes, kout, vout
+        del k, v, copies, kout, vout
     return out
 
 

@@ -1519,8 +1519,9 @@ __global__ __launch_bounds__(256) void decode_attn_combine_wide_kernel(AttnArgs 
   }
 }
 
-// Merge kernel choice: the per-row kernel reads a row's splits serially, the
-// wide one spreads them over a block (worth it once there are many splits).
+// Merge kernel choice: the per-row kernel gives a row's splits to one set of
+// lanes, the wide one spreads them over a block (worth it once there are
+// many splits).
 template <int D>
 static void launch_combine(const AttnArgs& a, hipStream_t st) {
   const int rows = a.batch * a.n_queries * a.n_q_heads;
