@@ -136,7 +136,7 @@ def test_full_size_decode_pairs():
     rest = [(b, g) for b in range(1, B - 1) for g in range(Hkv)]
     pairs += [rest[i] for i in rng.choice(len(rest), size=16, replace=False)]
     rep = Hq // Hkv
-    worst = {"max_rel_l2": 0.0, "max_abs_err": 0.0}
+    worst = {"max_rel_l2": 0.0, "max_rel_l2_bf16_floor": 0.0, "max_abs_err": 0.0}
     kt = vt = 0
     for i, (b, g) in enumerate(pairs):
         kr = synth.bf16_bits(k[b, :, g]).reshape(-1, d)
@@ -158,7 +158,7 @@ def test_full_size_decode_pairs():
             _say(f"[gpu attn] full size pair {i + 1}/{len(pairs)} (b={b}, kv head {g}): {st}")
     record(f"decode attention k8v3 d128 (B{B} Hq{Hq} Hkv{Hkv} ctx{N}, {len(pairs)} of {B * Hkv} pairs)",
            rows=len(pairs) * N, key_ties=kt, value_ties=vt, max_rel_l2=worst["max_rel_l2"],
-           max_abs_err=worst["max_abs_err"])
+           max_rel_l2_bf16_floor=worst["max_rel_l2_bf16_floor"], max_abs_err=worst["max_abs_err"])
     _say(f"[gpu attn] full size decode: {len(pairs)} pairs, ties k={kt} v={vt}, worst {worst}")
 
 
