@@ -272,3 +272,43 @@ def test_grow_validation_errors_without_gpu():
     assert call(batch=0) == 0
     assert call(dst_capacity=0) == 0
     assert tq.status_string(-9).startswith("an output buffer overlaps")
+
+
+def _attn_splits(d, kb, vb, B, M, Hq, Hkv, N):
+    ws = tq.tq_attn_quant_workspace_bytes(tq.scheme(d, kb, vb), B, M, Hq, Hkv, N)
+    per = B * M * Hq * (d + 4) * 4
+    assert ws % per == 0
+    return ws // per
+
+
+@pytest.mark.parametrize("d,kb,vb,B,M,Hq,Hkv,N,splits", [
+    # the bench's decode: 128 (sequence, kv head) units of four rows, four splits: 512 blocks
+    (128, 8, 3, 16, 1, 32, 8, 32768, 4),
+    # launch-bound single sequences: enough splits to reach 256 blocks, a step or two each
+    (128, 8, 3, 1, 1, 32, 8, 2048, 16), (128, 8, 3, 1, 1, 32, 8, 8192, 32),
+    (128, 8, 3, 1, 1, 16, 4, 8192, 64),
+    # GQA 6 at d256: one 16-row tile per kv head, 4 units, 64 splits
+    (256, 8, 3, 1, 1, 24, 4, 16384, 64),
+    # four queries per sequence: one 16-row tile per kv head
+    (128, 8, 3, 16, 4, 32, 8, 32768, 4),
+    # 40 units: 13 splits of 640 tokens
+    (128, 8, 3, 5, 1, 32, 8, 8192, 13),
+    # a context shorter than one step: one split
+    (128, 8, 3, 2, 1, 32, 8, 100, 1),
+    # the VALU kernel (d512, 16 tokens per block pass): 2048 blocks aimed at,
+    # one pass per split, 163 splits of 16 tokens
+    (512, 5, 2, 1, 1, 8, 2, 2600, 163),
+])
+def test_attention_split_geometry(d, kb, vb, B, M, Hq, Hkv, N, splits):
+    # host logic only: the split count the workspace size implies
+    assert _attn_splits(d, kb, vb, B, M, Hq, Hkv, N) == splits
+
+
+def test_attention_splits_cover_the_context():
+    # every split count keeps at least one token per split at max_ctx (no
+    # split past the context) over a sweep of shapes
+    for d, kb, vb in ((128, 8, 3), (256, 4, 4), (64, 8, 3), (512, 5, 2)):
+        for B, Hq, Hkv in ((1, 8, 8), (3, 32, 8), (16, 32, 8), (64, 8, 1)):
+            for N in (1, 31, 128, 1000, 4096, 32768):
+                s = _attn_splits(d, kb, vb, B, 1, Hq, Hkv, N)
+                assert 1 <= s <= N
