@@ -37,7 +37,7 @@ def _log(msg):
 KERNEL_SOURCES = {"quantize_kernel": "tq_codec.hip", "dequantize_kernel": "tq_codec.hip",
                   "decode_attn_mfma_kernel": "tq_attn.hip", "dense_quantize_kernel": "tq_dense.hip",
                   "dense_dequantize_kernel": "tq_dense.hip"}
-SHARED_HEADERS = ("tq_codebooks.h", "tq_device.h", "tq_launch.h")
+SHARED_HEADERS = ("tq_codebooks.h", "tq_device.h", "tq_launch.h", "tq_check.h")
 
 
 def source_hash(kernel: str) -> str:

@@ -371,6 +371,27 @@ int32_t tq_dense_dequantize(const tq_dense_scheme* scheme, const tq_dense_planes
                             const uint16_t* rot_bf16, const uint16_t* proj_bf16, uint16_t* x_bf16,
                             const tq_rows* out_rows, void* stream);
 
+/* ---- Checked build (for tests and debugging; no passage defines it).
+ * libtq_check.so is these sources built with TQ_CHECK: every kernel tests
+ * the global rows, records and byte offsets it derives against the extents
+ * the host computes for each buffer from the call's own arguments (row
+ * maps, capacities, counts, workspace geometry).  A failed test sets a bit
+ * in a device flag word (no trap) and keeps the access in range: a store is
+ * dropped, a load reads the buffer's first row.  Host only. */
+
+/* Waits for the current device, then returns the OR of the flag bits set
+ * since the last call (0: every access was in range) and clears them.
+ * Returns -1 in the library built without TQ_CHECK, TQ_E_HIP if the device
+ * could not be read. */
+int64_t tq_check_flags(void);
+
+/* Positive control of the checks: every extent handed to the kernels is
+ * reduced by `margin` rows (bytes for tq_grow_kv) until set back to 0, so
+ * that a call covering its buffers to the end must set flags.  Process-wide.
+ * Returns TQ_OK, TQ_E_SHAPE for a negative margin, or -1 in the library
+ * built without TQ_CHECK. */
+int64_t tq_check_set_margin(int64_t margin);
+
 /* Static description of a status code (the TQ_E_* codes above; the pages
  * ask that unsupported head dims be refused up front, TurboQuant page,
  * "Architecture in mlx-bun").  Host only. */

@@ -1,4 +1,6 @@
-"""Build libtq.so (the HIP codec library) in-tree for gfx950.
+"""Build libtq.so (the HIP codec library) and libtq_check.so (the same
+sources with every kernel's bounds tests compiled in, TQ_CHECK) in-tree for
+gfx950.
 
     python -m kv_cache_quantization_02_amd.build
 """
@@ -11,6 +13,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtq.so")
+LIB_CHECK = os.path.join(PKG, "libtq_check.so")
+# library -> extra flags
+VARIANTS = {LIB: [], LIB_CHECK: ["-DTQ_CHECK"]}
 SOURCES = ["tq_api.hip", "tq_codec.hip", "tq_attn.hip", "tq_dense.hip", "tq_cache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -35,20 +40,27 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source to an object (in parallel), then link libtq.so."""
+    """Compile every source of both libraries to objects (in parallel), then
+    link each; returns the path of libtq.so."""
     from concurrent.futures import ThreadPoolExecutor
 
-    objs = [LIB + "." + os.path.splitext(s)[0] + ".o" for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, *SOURCE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
-            for s, o in zip(SOURCES, objs)]
-    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
-        results = list(ex.map(_run, cmds))
-    tmp = LIB + ".tmp"
+    jobs = []  # (library, object, command)
+    for lib, extra in VARIANTS.items():
+        for src in SOURCES:
+            obj = lib + "." + os.path.splitext(src)[0] + ".o"
+            jobs.append((lib, obj, [HIPCC, *FLAGS, *extra, *SOURCE_FLAGS.get(src, []), "-c",
+                                    os.path.join(CSRC, src), "-o", obj]))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        results = list(ex.map(_run, [cmd for _, _, cmd in jobs]))
+    links = []
     if all(r.returncode == 0 for r in results):
-        results.append(_run([HIPCC, *FLAGS, "-shared", *objs, "-o", tmp]))
-    for o in objs:
-        if os.path.exists(o):
-            os.remove(o)
+        for lib in VARIANTS:
+            objs = [obj for l, obj, _ in jobs if l == lib]
+            links.append((lib, _run([HIPCC, *FLAGS, "-shared", *objs, "-o", lib + ".tmp"])))
+    for _, obj, _ in jobs:
+        if os.path.exists(obj):
+            os.remove(obj)
+    results += [r for _, r in links]
     failed = [r for r in results if r.returncode != 0]
     noise = "is not a recognized feature for this target"
     for r in (failed if failed else (results if verbose else [])):
@@ -56,8 +68,9 @@ def build(verbose: bool = False) -> str:
         if msg.strip():
             sys.stderr.write(msg + "\n")
     if failed:
-        raise RuntimeError("hipcc failed building libtq.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError("hipcc failed building libtq.so / libtq_check.so")
+    for lib, _ in links:
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 

@@ -2,6 +2,7 @@
 // row-index set-up and kernel dispatch.  Nothing here allocates.
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/tq.h"
@@ -77,6 +78,24 @@ bool same_counts(const tq_rows* a, const tq_rows* b) {
 }
 
 tq::RowMap map_of(const tq_rows* r) { return tq::RowMap{r->seq_stride, r->tok_stride, r->head_stride}; }
+
+// The checked build's positive control: rows (bytes, for growth) taken off
+// every extent handed to the kernels (tq_check_set_margin).
+std::atomic<int64_t> g_check_margin{0};
+
+int64_t shrink(int64_t e) {
+  if (!tq::kChecked) return e;
+  const int64_t m = g_check_margin.load();
+  return e > m ? e - m : 0;
+}
+
+// Rows a map addresses, as handed to the kernels' bounds tests.
+int64_t ext_of(int64_t n_seq, int64_t n_tok, int64_t n_head, int64_t ss, int64_t ts, int64_t hs) {
+  return shrink(tq::map_extent(n_seq, n_tok, n_head, ss, ts, hs));
+}
+int64_t ext_of(const tq_rows* r) {
+  return ext_of(r->n_seq, r->n_tok, r->n_head, r->seq_stride, r->tok_stride, r->head_stride);
+}
 
 int32_t check_planes(const tq_planes* p) {
   if (!p) return TQ_E_NULL;
@@ -164,6 +183,8 @@ int32_t tq_quantize_kv(const tq_scheme* s, const uint16_t* k_bf16, const uint16_
   a.split = split;
   a.in = map_of(in_rows);
   a.out = map_of(out_rows);
+  a.in_ext = ext_of(in_rows);
+  a.out_ext = ext_of(out_rows);
   return hip_status(tq::launch_quantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
                                         kMaxCodecBlocks));
 }
@@ -197,6 +218,8 @@ int32_t tq_dequantize_kv(const tq_scheme* s, const tq_planes* in, const tq_rows*
   a.split = split;
   a.in = map_of(in_rows);
   a.out = map_of(out_rows);
+  a.in_ext = ext_of(in_rows);
+  a.out_ext = ext_of(out_rows);
   return hip_status(tq::launch_dequantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
                                           kMaxCodecBlocks));
 }
@@ -234,6 +257,9 @@ int32_t tq_append_kv(const tq_scheme* s, const uint16_t* k_bf16, const uint16_t*
   a.out = map_of(&out);
   a.out_pos = positions;
   a.out_cap = capacity;
+  a.in_ext = ext_of(&in);
+  // tokens land at positions[b] + j within [0, capacity)
+  a.out_ext = ext_of(batch, capacity, n_kv_heads, seq_stride_rows, 1, head_stride_rows);
   return hip_status(tq::launch_quantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
                                         kMaxCodecBlocks));
 }
@@ -275,6 +301,9 @@ int32_t tq_fetch_kv(const tq_scheme* s, const tq_planes* cache, int32_t batch, i
   a.out = map_of(&out);
   a.in_len = lens;
   a.in_cap = capacity;
+  // tokens read lie below min(lens[b], capacity, window)
+  a.in_ext = ext_of(batch, n_kv_heads, window < capacity ? window : capacity, seq_stride_rows, head_stride_rows, 1);
+  a.out_ext = ext_of(&out);
   a.rotated = values_rotated ? 1 : 0;
   return hip_status(tq::launch_dequantize(a, s->head_dim, s->k_bits, s->v_bits, (hipStream_t)stream,
                                           kMaxCodecBlocks));
@@ -373,6 +402,8 @@ int32_t tq_grow_kv(const tq_scheme* s, int32_t batch, int32_t n_kv_heads, const 
     g.chunks = (uint32_t)chunks;
     g.vec16 = aligned16(sp[p]) && aligned16(dp[p]) && g.src_seq % 16 == 0 && g.src_head % 16 == 0 &&
               g.dst_seq % 16 == 0 && g.dst_head % 16 == 0;
+    g.src_ext = shrink((int64_t)(rd[p].hi - rd[p].lo));
+    g.dst_ext = shrink((int64_t)(wr[p].hi - wr[p].lo));
     a.first[p] = (uint32_t)total;
     total += (uint64_t)batch * (uint64_t)n_kv_heads * chunks;
     if (total > UINT32_MAX) return TQ_E_SHAPE;
@@ -405,6 +436,8 @@ int32_t tq_unrotate_rows(int32_t head_dim, const uint16_t* in_bf16, const tq_row
   a.split = split;
   a.in_map = map_of(in_rows);
   a.out_map = map_of(out_rows);
+  a.in_ext = ext_of(in_rows);
+  a.out_ext = ext_of(out_rows);
   return hip_status(tq::launch_unrotate(a, head_dim, (hipStream_t)stream, kMaxCodecBlocks));
 }
 
@@ -474,6 +507,7 @@ int32_t attn_prepare(const tq_scheme* s, const uint16_t* q_bf16, int32_t batch, 
   a->tokens_per_split = tps;
   a->softmax_scale = softmax_scale;
   a->n_queries = n_queries;
+  a->cache_ext = ext_of(batch, n_kv_heads, max_ctx, seq_stride_rows, head_stride_rows, 1);
   return TQ_OK;
 }
 
@@ -602,6 +636,8 @@ int32_t check_dense_call(const tq_dense_scheme* s, const uint16_t* x, const uint
   a->split = split;
   a->x_map = map_of(x_rows);
   a->plane_map = map_of(p_rows);
+  a->x_ext = ext_of(x_rows);
+  a->plane_ext = ext_of(p_rows);
   return TQ_OK;
 }
 
@@ -629,6 +665,21 @@ int32_t tq_dense_dequantize(const tq_dense_scheme* s, const tq_dense_planes* in,
   if (a.rows == 0) return TQ_OK;
   a.x_out = x_bf16;
   return hip_status(tq::launch_dense_dequantize(a, s->head_dim, s->bits, s->qjl != 0, (hipStream_t)stream));
+}
+
+int64_t tq_check_flags(void) {
+  if (!tq::kChecked) return -1;
+  if (hipDeviceSynchronize() != hipSuccess) return TQ_E_HIP;
+  const uint32_t v = tq::check_read_clear_codec() | tq::check_read_clear_attn() | tq::check_read_clear_cache() |
+                     tq::check_read_clear_dense();
+  return (int64_t)v;
+}
+
+int64_t tq_check_set_margin(int64_t margin) {
+  if (!tq::kChecked) return -1;
+  if (margin < 0) return TQ_E_SHAPE;
+  g_check_margin.store(margin);
+  return TQ_OK;
 }
 
 const char* tq_status_string(int32_t status) {

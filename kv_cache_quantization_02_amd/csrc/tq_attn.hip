@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPR, c = lane / LPR;
 
-  int ctx = a.ctx_lens[b];
+  int ctx = a.ctx_lens[check_row(b, a.batch, kChkAttnLen)];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   const int t_begin = split * a.tokens_per_split;
   int t_end = t_begin + a.tokens_per_split;
@@ -97,8 +97,9 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
     hv[j] = jr < nrow;
     const int mq = hv[j] ? jr / rep : 0, hq = g * rep + (hv[j] ? jr % rep : 0);
     lim[j] = ctx - a.n_queries + 1 + mq;
-    const uint4 w = *reinterpret_cast<const uint4*>(
-        a.q + (((int64_t)b * a.n_queries + mq) * a.n_q_heads + hq) * D + 8 * sub);
+    const int64_t qr = check_row(((int64_t)b * a.n_queries + mq) * a.n_q_heads + hq,
+                                 (int64_t)a.batch * a.n_queries * a.n_q_heads, kChkAttnQ);
+    const uint4 w = *reinterpret_cast<const uint4*>(a.q + qr * D + 8 * sub);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
       const bool valid = t < t_end;
       float kh[8];
       if (valid) {
-        const int64_t row = row0 + t;
+        const int64_t row = check_row(row0 + t, a.cache_ext, kChkAttnCache);
         const uint64_t bits = load_lane_bits<KB>(a.k_q + row * KROW, sub);
         const float s16 = f16_value(a.k_scale[row * G + (sub >> 2)]);
         const float z16 = f16_value(a.k_zero[row * G + (sub >> 2)]);
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
     for (int k = 0; k < kChunk; ++k) {
       const int t = t0 + k * TPW + c;
       if (t < t_end) {
-        const int64_t row = row0 + t;
+        const int64_t row = check_row(row0 + t, a.cache_ext, kChkAttnCache);
         const uint64_t bits = load_lane_bits<VB>(a.v_q + row * VROW, sub);
         const float vs = f16_value(a.v_scale[row * G + (sub >> 2)]);
         float z[8];
@@ -219,7 +220,9 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
         }
     }
     const int64_t orow = ((int64_t)b * a.n_queries + jr / rep) * a.n_q_heads + g * rep + jr % rep;
-    float* part = a.part + (orow * a.splits + split) * part_stride<D>();
+    const int64_t rec = orow * a.splits + split;
+    if (!check_ok(rec < (int64_t)a.batch * a.n_queries * a.n_q_heads * a.splits, kChkAttnPart)) continue;
+    float* part = a.part + rec * part_stride<D>();
     part[e] = aa;
     if (e == 0) {
       part[D] = mm;
@@ -524,6 +527,9 @@ __device__ __forceinline__ void centroid_operands(const lds_u32* const (&f)[8], 
 template <int D, int KB, int VB, bool TAIL>
 __device__ __forceinline__ void attn_dma(const AttnArgs& a, lds_u8* stage, int64_t r0, int tl, int lane) {
   using C = MfmaCfg<D, KB, VB>;
+  // the step's rows r0 .. r0 + (TAIL ? tl : CH) - 1 (checked build: a step
+  // past the cache's extent copies its first rows instead)
+  if (!check_ok(r0 + (TAIL ? tl : C::CH) <= a.cache_ext, kChkAttnCache)) r0 = 0;
   const uint8_t* kb = a.k_q + r0 * C::KRB;
 #pragma unroll
   for (int j = 0; j < C::NK; ++j) {
@@ -722,7 +728,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   fill_centroid_lut<VB>(lds_all);
   if (lane < 32) pb[C::PB + lane] = 0.f;
 
-  int ctx = a.ctx_lens[b];
+  int ctx = a.ctx_lens[check_row(b, a.batch, kChkAttnLen)];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   const int t_begin = split * a.tokens_per_split;
   int t_end = t_begin + a.tokens_per_split;
@@ -746,7 +752,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   auto qhead = [&](int h) -> const uint16_t* {
     const int jr = tile * kHeadTile + h;
     const int mq = jr < nrow ? jr / rep : 0, hq = gkv * rep + (jr < nrow ? jr % rep : 0);
-    return a.q + (((int64_t)b * a.n_queries + mq) * a.n_q_heads + hq) * D;
+    return a.q + check_row(((int64_t)b * a.n_queries + mq) * a.n_q_heads + hq,
+                           (int64_t)a.batch * a.n_queries * a.n_q_heads, kChkAttnQ) * D;
   };
   auto hvalid = [&](int h) { return tile * kHeadTile + h < nrow; };
   // per-head power of two (lane-group c measures head c)
@@ -1029,7 +1036,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     const int jr = tile * kHeadTile + h;
     const int64_t orow = ((int64_t)b * a.n_queries + jr / rep) * a.n_q_heads + gkv * rep + jr % rep;
-    float* part = a.part + (orow * a.splits + split) * part_stride<D>();
+    const int64_t rec = orow * a.splits + split;
+    if (!check_ok(rec < (int64_t)a.batch * a.n_queries * a.n_q_heads * a.splits, kChkAttnPart)) continue;
+    float* part = a.part + rec * part_stride<D>();
     part[e] = aa;
     if (e == 0) {
       part[D] = mm;
@@ -1106,7 +1115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
   fill_centroid_lut<VB>(lds_all);
 
-  int ctx = a.ctx_lens[b];
+  int ctx = a.ctx_lens[check_row(b, a.batch, kChkAttnLen)];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   const int t_begin = split * a.tokens_per_split;
   int t_end = t_begin + a.tokens_per_split;
@@ -1127,7 +1136,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int jr = tile * R + n;
   const bool rv = jr < nrow;
   const int mq = rv ? jr / rep : 0;
-  const uint16_t* const qrow = a.q + (((int64_t)b * a.n_queries + mq) * a.n_q_heads + gkv * rep + (rv ? jr % rep : 0)) * D;
+  const uint16_t* const qrow =
+      a.q + check_row(((int64_t)b * a.n_queries + mq) * a.n_q_heads + gkv * rep + (rv ? jr % rep : 0),
+                      (int64_t)a.batch * a.n_queries * a.n_q_heads, kChkAttnQ) * D;
   // this lane's query elements: 32g + 8c + [0, 8) of every group g
   uint4 qw[G];
   float qmax = 0.f;
@@ -1347,7 +1358,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       }
     }
     const int64_t orow = ((int64_t)b * a.n_queries + jh / rep) * a.n_q_heads + gkv * rep + jh % rep;
-    float* part = a.part + (orow * a.splits + split) * part_stride<D>();
+    const int64_t rec = orow * a.splits + split;
+    if (!check_ok(rec < (int64_t)a.batch * a.n_queries * a.n_q_heads * a.splits, kChkAttnPart)) continue;
+    float* part = a.part + rec * part_stride<D>();
     part[e] = aa;
     if (e == 0) {
       part[D] = mm;
@@ -1457,7 +1470,7 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
     o.y = pack_bf16x2(acc[2], acc[3]);
     o.z = pack_bf16x2(acc[4], acc[5]);
     o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(a.out + (int64_t)r * D + 8 * sub) = o;
+    if (check_ok(r < rows, kChkAttnOut)) *reinterpret_cast<uint4*>(a.out + (int64_t)r * D + 8 * sub) = o;
   }
 }
 
@@ -1515,9 +1528,11 @@ __global__ __launch_bounds__(256) void decode_attn_combine_wide_kernel(AttnArgs 
     o.y = pack_bf16x2(acc[2], acc[3]);
     o.z = pack_bf16x2(acc[4], acc[5]);
     o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(a.out + (int64_t)r * D + 8 * sub) = o;
+    if (check_ok(r < a.batch * a.n_queries * a.n_q_heads, kChkAttnOut)) *reinterpret_cast<uint4*>(a.out + (int64_t)r * D + 8 * sub) = o;
   }
 }
+
+uint32_t check_read_clear_attn() { return check_read_clear_file(); }
 
 // Merge kernel choice: the per-row kernel gives a row's splits to one set of
 // lanes, the wide one spreads them over a block (worth it once there are

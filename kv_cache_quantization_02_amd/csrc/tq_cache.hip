@@ -59,8 +59,18 @@ __global__ __launch_bounds__(kThreads) void grow_kernel(GrowArgs a) {
     const uint32_t chunk = r - seg * pl.chunks;
     const uint32_t b = seg / a.n_kv_heads;
     const uint32_t g = seg - b * a.n_kv_heads;
-    const uint8_t* src = pl.src + (int64_t)b * pl.src_seq + (int64_t)g * pl.src_head;
-    uint8_t* dst = pl.dst + (int64_t)b * pl.dst_seq + (int64_t)g * pl.dst_head;
+    int64_t so = (int64_t)b * pl.src_seq + (int64_t)g * pl.src_head;
+    int64_t dof = (int64_t)b * pl.dst_seq + (int64_t)g * pl.dst_head;
+    if (kChecked) {
+      // the segment's kept bytes and its whole destination inside the
+      // extents (a failed bound reads from and writes to nothing outside:
+      // the chunk is skipped)
+      const bool ok = check_ok(so + pl.copy <= pl.src_ext, kChkGrowSrc) &
+                      check_ok(dof + pl.dst_bytes <= pl.dst_ext, kChkGrowDst);
+      if (!ok) continue;
+    }
+    const uint8_t* src = pl.src + so;
+    uint8_t* dst = pl.dst + dof;
     const int64_t x0 = (int64_t)chunk * kGrowChunkBytes;
     if (pl.vec16 && x0 + kGrowChunkBytes <= pl.copy) {
       // a chunk of kept rows: every load of the block issues before its
@@ -97,6 +107,8 @@ __global__ __launch_bounds__(kThreads) void grow_kernel(GrowArgs a) {
 }
 
 }  // namespace
+
+uint32_t check_read_clear_cache() { return check_read_clear_file(); }
 
 hipError_t launch_grow(const GrowArgs& a, hipStream_t st, int max_blocks) {
   if (a.total == 0) return hipSuccess;

@@ -214,16 +214,19 @@ __device__ __forceinline__ int32_t load_i32_now(const int32_t* p) {
 // past the end or falls outside the cache window of an append.
 __device__ __forceinline__ int64_t quant_out_row(const QuantArgs& a, uint32_t r, bool contig_out) {
   if (r >= a.rows) return -1;
-  if (contig_out) return r;
-  uint32_t s, t, h;
-  split_row(r, a.split, s, t, h);
-  int64_t o = row_index(a.out, s, t, h);
-  if (a.out_pos) {
-    const int64_t p = load_i32_now(a.out_pos + s);
-    if (p + t < 0 || p + t >= a.out_cap) return -1;
-    o += p * a.out.tok_stride;
+  int64_t o = r;
+  if (!contig_out) {
+    uint32_t s, t, h;
+    split_row(r, a.split, s, t, h);
+    o = row_index(a.out, s, t, h);
+    if (a.out_pos) {
+      const int64_t p = load_i32_now(a.out_pos + s);
+      if (p + t < 0 || p + t >= a.out_cap) return -1;
+      o += p * a.out.tok_stride;
+    }
   }
-  return o;
+  // a row outside the out map's extent is not written (checked build)
+  return check_ok(o < a.out_ext, kChkQuantOut) ? o : -1;
 }
 
 // Byte offset, within a contiguous tile, of copy slot 64j + lane.
@@ -252,7 +255,9 @@ __device__ __forceinline__ void tile_issue(const uint16_t* src, const QuantArgs&
                                            const uint32_t (&off)[4], const lds_u8* stage, int lane) {
   using L = GroupLanes<D>;
   if (contig && base + L::RPW <= a.rows) {
-    tile_issue_contig(src, base, D, off, stage);
+    // (a failed bound reads the first rows instead; the contiguous path
+    // implies at least RPW rows)
+    tile_issue_contig(src, check_ok(base + L::RPW <= a.in_ext, kChkQuantIn) ? base : 0u, D, off, stage);
     return;
   }
 #pragma unroll
@@ -266,6 +271,7 @@ __device__ __forceinline__ void tile_issue(const uint16_t* src, const QuantArgs&
       split_row(r, a.split, s, t, h);
       irow = row_index(a.in, s, t, h);
     }
+    irow = check_row(irow, a.in_ext, kChkQuantIn);
     tile_copy16(src + irow * D + kGroup * L::group(reader) + 8 * q, stage + 1024 * j);
   }
 }
@@ -638,6 +644,11 @@ __device__ __forceinline__ void pass_rows(const DequantArgs& a, uint32_t base, u
     split_row(act[u] ? r : 0u, a.split, s, t, h);
     irow[u] = row_index(a.in, s, t, h);
     orow[u] = row_index(a.out, s, t, h);
+    if (kChecked && act[u]) {
+      // rows outside the extents: nothing is written, the first row is read
+      act[u] = check_ok(orow[u] < a.out_ext, kChkDequantOut);
+      if (!a.in_len) irow[u] = check_row(irow[u], a.in_ext, kChkDequantIn);
+    }
     // computed here, before the pass's loads: left to the compiler, this
     // arithmetic sinks below them, and its 64-bit temporaries then share
     // registers with loaded values, which makes the first use of any row
@@ -656,6 +667,7 @@ __device__ __forceinline__ void pass_rows(const DequantArgs& a, uint32_t base, u
     static_for<kBatch>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       live[u] = act[u] && (int64_t)tok[u] < min((int64_t)len[u], (int64_t)a.in_cap);
+      if (kChecked && live[u]) irow[u] = check_row(irow[u], a.in_ext, kChkDequantIn);
     });
   }
 }
@@ -983,7 +995,9 @@ __global__ __launch_bounds__(256) void unrotate_kernel(UnrotateArgs a) {
     const bool act = r < a.rows;
     uint32_t s, t, h;
     split_row(act ? r : 0u, a.split, s, t, h);
-    const int64_t irow = row_index(a.in_map, s, t, h), orow = row_index(a.out_map, s, t, h);
+    const int64_t irow = check_row(row_index(a.in_map, s, t, h), a.in_ext, kChkUnrotIn);
+    const int64_t orow = row_index(a.out_map, s, t, h);
+    const bool put = act && check_ok(orow < a.out_ext, kChkUnrotOut);
     uint32_t u[16];
     if (act) {
       load_group(a.in + irow * D + kGroup * g, u);
@@ -1003,7 +1017,7 @@ __global__ __launch_bounds__(256) void unrotate_kernel(UnrotateArgs a) {
     for (int i = 0; i < 16; ++i) {
       o[i] = canon_bf16x2(pack_bf16x2(w[2 * i] * m, w[2 * i + 1] * m) ^ smask[i]);
     }
-    store_tile<D>(o, a.out, act ? orow * D : -1, tile, offs, lane, g, rw);
+    store_tile<D>(o, a.out, put ? orow * D : -1, tile, offs, lane, g, rw);
   }
 }
 
@@ -1020,6 +1034,8 @@ hipError_t launch_unrotate(const UnrotateArgs& a, int d, hipStream_t st, int max
   }
   return hipGetLastError();
 }
+
+uint32_t check_read_clear_codec() { return check_read_clear_file(); }
 
 hipError_t launch_dequantize(const DequantArgs& a, int d, int kb, int vb, hipStream_t st, int max_blocks) {
   switch (d) {

@@ -306,8 +306,10 @@ __global__ __launch_bounds__(256) void dense_quantize_kernel(DenseArgs a) {
       adst[c] = r < a.rows;
       uint32_t s, t, h;
       split_row(adst[c] ? r : 0u, a.split, s, t, h);
-      const int64_t xo = row_index(a.x_map, s, t, h);
+      const int64_t xo = check_row(row_index(a.x_map, s, t, h), a.x_ext, kChkDenseIn);
       pdst[c] = row_index(a.plane_map, s, t, h);
+      // a plane row outside the extent is not written (checked build)
+      if (kChecked && adst[c]) adst[c] = check_ok(pdst[c] < a.plane_ext, kChkDenseOut);
       // chunk kc: coordinates 32 kc + 8 g + [0, 8), so the four lane-groups
       // of a row read 64 contiguous bytes per instruction
       const uint16_t* src = a.x + xo * D + 8 * g;
@@ -611,7 +613,9 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
       uint32_t s, t, h;
       split_row(act ? r : 0u, a.split, s, t, h);
       xo[c] = row_index(a.x_map, s, t, h);
-      const int64_t po = row_index(a.plane_map, s, t, h);
+      const int64_t po = check_row(row_index(a.plane_map, s, t, h), a.plane_ext, kChkDenseIn);
+      // an output row outside the extent is marked -1 and not written (checked build)
+      if (kChecked && act && !check_ok(xo[c] < a.x_ext, kChkDenseOut)) xo[c] = -1;
       if (act) {
         const uint8_t* irow = a.idx + po * (D * B / 8);
 #pragma unroll
@@ -736,6 +740,7 @@ __global__ __launch_bounds__(256) void dense_dequantize_kernel(DenseArgs a) {
         const int64_t row_off = (int64_t)(((uint64_t)hi32 << 32) | lo32);
         const float f = QJL ? 1.f : __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(scale[c])));
         if (tile * C::RW + 16 * c + src >= a.rows) continue;
+        if (kChecked && row_off < 0) continue;
         uint16_t* row = a.x_out + row_off * D + NT * n;
         if constexpr (NT >= 8) {
 #pragma unroll
@@ -832,6 +837,8 @@ hipError_t dense_dequant_d(const DenseArgs& a, int bits, bool qjl, hipStream_t s
 }
 
 }  // namespace
+
+uint32_t check_read_clear_dense() { return check_read_clear_file(); }
 
 hipError_t launch_dense_quantize(const DenseArgs& a, int d, int bits, bool qjl, hipStream_t st) {
   switch (d) {

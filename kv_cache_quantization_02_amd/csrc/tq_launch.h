@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tq_check.h"
 #include "tq_device.h"
 
 namespace tq {
@@ -44,6 +45,9 @@ struct QuantArgs {
   // out-row (s, out_pos[s] + t, h), and only when 0 <= out_pos[s] + t < out_cap.
   const int32_t* out_pos;
   int32_t out_cap;
+  // rows the in and out maps address (the checked build's bounds; with
+  // out_pos, the out map over the capacity)
+  int64_t in_ext, out_ext;
 };
 
 struct DequantArgs {
@@ -66,6 +70,8 @@ struct DequantArgs {
   int32_t in_cap;
   // Values left in the rotated domain: centroid * scale16, no transform or signs.
   int32_t rotated;
+  // rows the in map (over the capacity in a fetch) and the out map address
+  int64_t in_ext, out_ext;
 };
 
 struct AttnArgs {
@@ -89,6 +95,8 @@ struct AttnArgs {
   // wide layout is 16-byte aligned (value and key scale/zero planes at
   // 16-byte boundaries, even row strides).
   int32_t wide;
+  // cache rows the strides address over max_ctx tokens (checked build)
+  int64_t cache_ext;
 };
 
 // Inverse rotation of bf16 rows: out = bf16(signs * FWHT(in) / sqrt(d)).
@@ -99,6 +107,7 @@ struct UnrotateArgs {
   uint32_t rows;
   RowSplit split;
   RowMap in_map, out_map;
+  int64_t in_ext, out_ext;  // rows each map addresses (checked build)
 };
 
 // Paper variant (dense rotation, one norm per row, optional QJL residual).
@@ -116,6 +125,7 @@ struct DenseArgs {
   uint32_t rows;
   RowSplit split;
   RowMap x_map, plane_map;
+  int64_t x_ext, plane_ext;  // rows each map addresses (checked build)
 };
 
 // Re-laying a cache at another capacity.  Each plane is a set of
@@ -129,6 +139,7 @@ struct GrowPlane {
   int64_t copy, dst_bytes;
   uint32_t chunks;  // blocks per segment
   uint32_t vec16;   // every segment start 16-byte aligned on both sides
+  int64_t src_ext, dst_ext;  // bytes the segments span on each side (checked build)
 };
 
 struct GrowArgs {

@@ -312,3 +312,23 @@ def test_attention_splits_cover_the_context():
             for N in (1, 31, 128, 1000, 4096, 32768):
                 s = _attn_splits(d, kb, vb, B, 1, Hq, Hkv, N)
                 assert 1 <= s <= N
+
+
+def test_checked_build_loads_without_gpu():
+    # the production library answers -1 (no bounds tests compiled in)
+    assert tq.tq_check_flags() == -1
+    assert tq.tq_check_set_margin(0) == -1
+    # the checked build exports the same entry points and validates the margin
+    L = tq.load(tq.CHECKED_LIB_PATH)
+    missing = sorted(n for n in _declared_functions() if not hasattr(L, n))
+    assert not missing, missing
+    assert L.tq_check_set_margin(-1) == -4
+    assert L.tq_check_set_margin(0) == 0
+    # host validation is the same code in both builds
+    sch = tq.scheme(100, 8, 3)
+    assert L.tq_check_scheme(ctypes.byref(sch)) == lib_status("TQ_E_HEAD_DIM")
+
+
+def lib_status(name):
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return int(re.search(rf"#define {name} \(?(-?\d+)\)?", text).group(1))
