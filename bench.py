@@ -547,7 +547,7 @@ def main():
         "dequantize": {"kernel": "dequantize_kernel<128,8,3>", "us": phase_ms["dequantize"] * 1e3,
                        "token_heads_per_s": rows_q / (phase_ms["dequantize"] * 1e-3),
                        "GBps": bytes_dq / (phase_ms["dequantize"] * 1e-3) / 1e9},
-        "decode_attn": {"kernel": "decode_attn_mfma_kernel<128,3> + combine",
+        "decode_attn": {"kernel": "decode_attn_mfma_kernel<128,8,3> + combine",
                         "us": phase_ms["decode_attn"] * 1e3,
                         "cache_token_heads_per_s": rows_a / (phase_ms["decode_attn"] * 1e-3),
                         "GBps": bytes_a / (phase_ms["decode_attn"] * 1e-3) / 1e9},
