@@ -1548,11 +1548,11 @@ static void launch_combine(const AttnArgs& a, hipStream_t st) {
   }
 }
 
-// int8 keys, and packed 5-, 4- and 2-bit keys spread into bytes (2- and
-// 5-bit rows of d = 64 do not keep the 16-byte alignment of the copies);
-// values of 2 to 5 bits
+// int8 keys, and packed 5-, 4- and 2-bit keys spread into bytes (5-bit rows
+// of d = 64, 40 bytes, do not keep the 16-byte alignment of the copies);
+// values of 2 to 5 and 8 bits
 bool decode_attn_uses_mfma(int d, int kb, int vb) {
-  return d <= 256 && (vb <= 5 || vb == 8) && (kb == 8 || kb == 4 || ((kb == 2 || kb == 5) && d >= 128));
+  return d <= 256 && (vb <= 5 || vb == 8) && (kb == 8 || kb == 4 || kb == 2 || (kb == 5 && d >= 128));
 }
 
 void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n_q_heads, int n_kv_heads,
@@ -1652,9 +1652,7 @@ static hipError_t launch_attn_d(const AttnArgs& a, int kb, int vb, hipStream_t s
                ((uintptr_t)a.k_zero & 15u) == 0 && (a.seq_stride & 1) == 0 && (a.head_stride & 1) == 0;
       const int nrow = a.n_queries * rep;
       switch (kb) {
-        case 2:
-          if constexpr (D >= 128) launch_mfma_kb<D, 2>(w, vb, nrow, grid, st);
-          break;
+        case 2: launch_mfma_kb<D, 2>(w, vb, nrow, grid, st); break;
         case 4: launch_mfma_kb<D, 4>(w, vb, nrow, grid, st); break;
         case 5:
           if constexpr (D >= 128) launch_mfma_kb<D, 5>(w, vb, nrow, grid, st);

@@ -241,6 +241,11 @@ def test_sixteen_row_tiles(B, M, Hq, Hkv, N, d, vb, ctx):
     (2, 2, 8, 2, 300, 64, 4, 8, [300, 77]),
     (1, 1, 32, 8, 9000, 128, 8, 4, [9000]),
     (2, 3, 8, 2, 300, 256, 8, 2, [300, 200]),
+    # 2-bit keys at d64: 16-byte key rows, one DMA instruction whose upper lanes re-read the last chunk
+    (2, 1, 8, 2, 300, 64, 2, 3, [300, 45]),
+    (1, 3, 16, 4, 333, 64, 2, 5, [333]),
+    (2, 1, 4, 1, 260, 64, 2, 8, [260, 31]),
+    (1, 1, 8, 2, 5000, 64, 2, 2, [4999]),
 ])
 def test_packed_keys_on_matrix_cores(B, M, Hq, Hkv, N, d, kb, vb, ctx):
     got, ref = run_mq_case(B, M, Hq, Hkv, N, d, kb, vb, ctx, 26, f"packed keys k{kb}v{vb} d{d} M{M} rep{Hq // Hkv}")
