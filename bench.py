@@ -136,12 +136,13 @@ def _time_us(fn, reps):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
-def _time_calls_us(fn, reps):
+def _time_calls_us(fn, reps, per_fn=False):
     """(mean, median) microseconds of `reps` back-to-back calls after one
     untimed pass, each call bracketed by its own pair of events.  `fn` is one
     callable or a list of them, called in rotation (each on its own copy of
     the data, so that rotating through copies larger than the 256 MB
-    last-level cache in total keeps every call reading HBM)."""
+    last-level cache in total keeps every call reading HBM).  With per_fn,
+    the median of each function's own calls follows."""
     import torch
     fns = fn if isinstance(fn, (list, tuple)) else [fn]
     for f in fns:
@@ -153,8 +154,15 @@ def _time_calls_us(fn, reps):
         fns[i % len(fns)]()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
-    return sum(t) / reps, (t[(reps - 1) // 2] + t[reps // 2]) / 2
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
+
+    def med(x):
+        x = sorted(x)
+        return (x[(len(x) - 1) // 2] + x[len(x) // 2]) / 2
+    out = (sum(per) / reps, med(per))
+    if per_fn:
+        out += tuple(med(per[k::len(fns)]) for k in range(len(fns)))
+    return out
 
 
 def _time_rotating_us(fns, reps):
@@ -214,6 +222,16 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
         assert st == 0, st
     us_e, med_e = _time_calls_us(lambda: fetch(False), 10)
     us_r, med_r = _time_calls_us(lambda: fetch(True), 10)
+    # the same bytes through the plain dequantize (the cache's rows as one
+    # contiguous block), its calls alternating with the eager fetch's so that
+    # both see the same clocks
+    rc = tq.contiguous_rows((B * Hkv * N, 1, 1))
+
+    def deq_same():
+        st = tq.tq_dequantize_kv(sch, planes, rc, sig, kw, vw, rc)
+        assert st == 0, st
+    pair = _time_calls_us([lambda: fetch(False), deq_same], 20, per_fn=True)
+    fetch_alt, deq_alt = pair[2], pair[3]
     fb = B * Hkv * N * (row_bytes + 4 * d)
     # un-rotate the rotated V window back to the original domain (into the K buffer)
     rws = tq.contiguous_rows((B * Hkv * N, 1, 1))
@@ -264,7 +282,10 @@ def measure_next_rows(tq, synth, sig, cache, B, Hkv, N, d, kb, vb, dev):
                       "us": us_a, "token_heads_per_s": rows / (us_a * 1e-6),
                       "GBps": rows * (4 * dd + tq.tq_row_bytes(tq.scheme(dd, akb, avb))) / (us_a * 1e-6) / 1e9},
         "fetch_kv_eager": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache",
-                           "us": us_e, "us_median": med_e, "GBps": fb / (us_e * 1e-6) / 1e9},
+                           "us": us_e, "us_median": med_e, "GBps": fb / (us_e * 1e-6) / 1e9,
+                           "alternating_with_dequantize": {
+                               "fetch_us_median": fetch_alt, "dequantize_same_bytes_us_median": deq_alt,
+                               "ratio": fetch_alt / deq_alt}},
         "fetch_kv_rotated": {"workload": f"full window of the {B}x{Hkv}x{N} k{kb}v{vb} cache, values rotated",
                              "us": us_r, "us_median": med_r, "GBps": fb / (us_r * 1e-6) / 1e9},
         "grow_kv": {"workload": f"the {B}x{Hkv}x{N} k{kb}v{vb} cache re-laid at capacity {Ng} "
