@@ -319,3 +319,21 @@ def test_many_splits_block_merge(Hq, Hkv, N, d, kb, vb, ctx):
     run_case(B, Hq, Hkv, N, d, kb, vb, ctx, 23, f"many splits d{d} k{kb}v{vb}")
     ws = tq.tq_decode_attn_workspace_bytes(sch, B, Hq, Hkv, N)
     assert ws >= 16 * B * Hq * (d + 4) * 4
+
+
+# Every GQA grouping from 1 to 16 query heads per kv head, one to five query
+# tokens per sequence: rows per kv head from 1 to 80, so tiles of four and of
+# 16 rows with every count of idle rows in the last tile; contexts that end on
+# a step boundary, one past it, and inside the first step.
+@pytest.mark.parametrize("rep", [1, 2, 3, 5, 7, 16])
+@pytest.mark.parametrize("M", [1, 2, 5])
+def test_gqa_groupings_and_query_counts(rep, M):
+    Hkv = 2
+    ctx = [257, 128, 33]
+    run_mq_case(3, M, rep * Hkv, Hkv, 257, 128, 8, 3, ctx, 31 + rep + 7 * M, f"rep{rep} M{M}")
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 3), (2, 4), (5, 2), (8, 8)])
+@pytest.mark.parametrize("rep", [3, 6])
+def test_gqa_groupings_packed_schemes(kb, vb, rep):
+    run_mq_case(2, 2, rep * 2, 2, 300, 128, kb, vb, [300, 129], 41 + kb + rep, f"k{kb}v{vb} rep{rep}")
