@@ -37,7 +37,11 @@ __device__ __forceinline__ const uint32_t* attn_centroids() {
 }
 
 constexpr int kHeadTile = 4;   // query heads per block
-constexpr int kChunk = 4;      // rows per lane-group between softmax rescales
+// Rows per lane-group between softmax rescales (VALU kernel).  Two rows and
+// 1024 blocks beat four rows and 2048 blocks by 12-30% (d = 512 k5v2 and k8v3
+// over a 16 x 8 x 4096 cache 316 / 395 -> 277 / 277 us; d = 64 k5v3 over
+// 16 x 8 x 16384 183 -> 145 us): fewer registers per wave and shorter chains.
+constexpr int kChunk = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;  // log2 slack of the matrix-core kernel's running maximum
 
@@ -1569,7 +1573,8 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   if (units < 1) units = 1;  // an empty batch: nothing runs, any split count serves
   // The matrix-core kernel streams through per-wave DMA stages, which pay a
   // pipeline fill per block: aim at one round of resident blocks (two per CU
-  // on the 256 CUs of gfx950).  The VALU kernel prefers more, shorter blocks.
+  // on the 256 CUs of gfx950).  The VALU kernel prefers four rounds of
+  // shorter blocks (1024: 512 and 4096 were slower).
   // Each split of the matrix-core kernel also keeps at least four steps per
   // wave, so that the fill is paid over several steps and the combine does
   // not merge dozens of tiny splits, but only while the grid still has 256
@@ -1577,7 +1582,7 @@ void decode_attn_geometry(int d, int kb, int vb, int batch, int n_queries, int n
   // of a step or two (one sequence, 8 kv heads, d = 128: 17.8 -> 13.5 us at
   // 2048 tokens, 18.6 -> 17.0 us at 8192; GQA 6 at d = 256 over 16384 tokens,
   // one 16-row tile per kv head: 32.5 -> 28.4 us).
-  const long long target = mfma ? 512 : 2048;
+  const long long target = mfma ? 512 : 1024;
   const long long min_steps = mfma ? 4 : 1;
   long long s = (target + units - 1) / units;
   long long max_s = (max_ctx + min_steps * step - 1) / (min_steps * step);

@@ -295,9 +295,9 @@ def _attn_splits(d, kb, vb, B, M, Hq, Hkv, N):
     (128, 8, 3, 5, 1, 32, 8, 8192, 13),
     # a context shorter than one step: one split
     (128, 8, 3, 2, 1, 32, 8, 100, 1),
-    # the VALU kernel (d512, 16 tokens per block pass): 2048 blocks aimed at,
-    # one pass per split, 163 splits of 16 tokens
-    (512, 5, 2, 1, 1, 8, 2, 2600, 163),
+    # the VALU kernel (d512, 8 tokens per block pass): 1024 blocks aimed at,
+    # one pass per split, 325 splits of 8 tokens
+    (512, 5, 2, 1, 1, 8, 2, 2600, 325),
 ])
 def test_attention_split_geometry(d, kb, vb, B, M, Hq, Hkv, N, splits):
     # host logic only: the split count the workspace size implies
