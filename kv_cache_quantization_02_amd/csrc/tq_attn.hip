@@ -1480,10 +1480,16 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
 
 // The same merge for many splits: one block per output row.  Slice k of the
 // block (LPR lanes) merges splits k, k + NSL, ... into (m_k, l_k, acc_k); the
-// slices then meet in LDS and the first LPR lanes finish the row.
+// slices then meet in LDS and the first LPR lanes finish the row.  At
+// d = 512 a row spans a whole wave, so the block has 16 waves (16 slices)
+// rather than 4: the VALU kernel's long single-sequence contexts reach 512
+// splits, which four slices would merge in 16 dependent batches each.
 template <int D>
-__global__ __launch_bounds__(256) void decode_attn_combine_wide_kernel(AttnArgs a) {
-  constexpr int LPR = D / 8, NSL = 256 / LPR;
+constexpr int combine_wide_threads() { return D >= 512 ? 1024 : 256; }
+
+template <int D>
+__global__ __launch_bounds__(1024) void decode_attn_combine_wide_kernel(AttnArgs a) {
+  constexpr int LPR = D / 8, NSL = combine_wide_threads<D>() / LPR;
   __shared__ float s_acc[NSL][D];
   __shared__ float s_ml[NSL][2];
   const int sub = threadIdx.x % LPR, k = threadIdx.x / LPR;
@@ -1545,7 +1551,7 @@ template <int D>
 static void launch_combine(const AttnArgs& a, hipStream_t st) {
   const int rows = a.batch * a.n_queries * a.n_q_heads;
   if (a.splits >= 16) {
-    decode_attn_combine_wide_kernel<D><<<dim3((unsigned)rows), 256, 0, st>>>(a);
+    decode_attn_combine_wide_kernel<D><<<dim3((unsigned)rows), combine_wide_threads<D>(), 0, st>>>(a);
   } else {
     const int rows_per_block = 4 * (64 / (D / 8));
     decode_attn_combine_kernel<D><<<dim3((rows + rows_per_block - 1) / rows_per_block), 256, 0, st>>>(a);
