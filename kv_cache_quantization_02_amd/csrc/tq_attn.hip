@@ -112,6 +112,16 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+  // per head, the sum of this lane's query elements: a lane's 8 key elements
+  // share one group's scale and zero, so its partial score is
+  // scale * (sum q * idx + zero * sum q)
+  float qs[kHeadTile];
+#pragma unroll
+  for (int j = 0; j < kHeadTile; ++j) {
+    qs[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qs[j] += q[j][i];
+  }
 
   float m[kHeadTile], l[kHeadTile], acc[kHeadTile][8];
 #pragma unroll
@@ -130,31 +140,29 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
     for (int k = 0; k < kChunk; ++k) {
       const int t = t0 + k * TPW + c;
       const bool valid = t < t_end;
-      float kh[8];
+      float kx[8], s16 = 0.f, z16 = 0.f;  // indices, the group's scale and zero
       if (valid) {
         const int64_t row = check_row(row0 + t, a.cache_ext, kChkAttnCache);
         const uint64_t bits = load_lane_bits<KB>(a.k_q + row * KROW, sub);
-        const float s16 = f16_value(a.k_scale[row * G + (sub >> 2)]);
-        const float z16 = f16_value(a.k_zero[row * G + (sub >> 2)]);
+        s16 = f16_value(a.k_scale[row * G + (sub >> 2)]);
+        z16 = f16_value(a.k_zero[row * G + (sub >> 2)]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float qi;
           if constexpr (KB == 8)
-            qi = (float)(int8_t)(bits >> (8 * i));
+            kx[i] = (float)(int8_t)(bits >> (8 * i));
           else
-            qi = (float)(uint32_t)((bits >> (KB * i)) & ((1u << KB) - 1));
-          kh[i] = (qi + z16) * s16;
+            kx[i] = (float)(uint32_t)((bits >> (KB * i)) & ((1u << KB) - 1));
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kh[i] = 0.f;
+        for (int i = 0; i < 8; ++i) kx[i] = 0.f;
       }
 #pragma unroll
       for (int j = 0; j < kHeadTile; ++j) {
         float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d = __builtin_fmaf(q[j][i], kh[i], d);
-        d = row_sum<D>(d);
+        for (int i = 0; i < 8; ++i) d = __builtin_fmaf(q[j][i], kx[i], d);
+        d = row_sum<D>(s16 * __builtin_fmaf(z16, qs[j], d));
         sc[k][j] = (valid && t < lim[j]) ? d : -INFINITY;
       }
     }
@@ -185,13 +193,16 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(AttnArgs a) {
         const int64_t row = check_row(row0 + t, a.cache_ext, kChkAttnCache);
         const uint64_t bits = load_lane_bits<VB>(a.v_q + row * VROW, sub);
         const float vs = f16_value(a.v_scale[row * G + (sub >> 2)]);
+        // the group's scale rides on the weights: p * scale, times the centroids
         float z[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) z[i] = cen_lds[(bits >> (VB * i)) & ((1u << VB) - 1)] * vs;
+        for (int i = 0; i < 8; ++i) z[i] = cen_lds[(bits >> (VB * i)) & ((1u << VB) - 1)];
 #pragma unroll
-        for (int j = 0; j < kHeadTile; ++j)
+        for (int j = 0; j < kHeadTile; ++j) {
+          const float pv = p[k][j] * vs;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[j][i] = __builtin_fmaf(p[k][j], z[i], acc[j][i]);
+          for (int i = 0; i < 8; ++i) acc[j][i] = __builtin_fmaf(pv, z[i], acc[j][i]);
+        }
       }
     }
   }
