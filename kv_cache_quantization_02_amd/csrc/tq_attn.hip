@@ -50,6 +50,15 @@ constexpr float kLazy = 8.0f;  // log2 slack of the matrix-core kernel's running
 template <int D>
 constexpr int part_stride() { return D + 4; }
 
+// x of another lane of the row, chosen by the DPP control CTRL
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// Sum over the D/8 lanes of a row, in every one of them.  The xor-4, -16 and
+// -32 steps go through the LDS crossbar (swizzle, bpermute): the VALU kernel
+// that uses this is bound by its VALU issue, and an all-VALU version (DPP
+// mirrors, permlane swaps) was 2-6% slower at d = 512.
 template <int D>
 __device__ __forceinline__ float row_sum(float v) {
   if constexpr (D >= 16) v += lane_xor<1>(v);
@@ -300,24 +309,19 @@ typedef __attribute__((address_space(3))) tq_i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) tq_float4 lds_f32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
 // all-reduce over the 16 lanes of a row (quad xor 1, xor 2, rotate 4, rotate 8)
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x124>(v));
-  v = fmaxf(v, dpp_f<0x128>(v));
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x124>(v));
+  v = fmaxf(v, dpp_mov<0x128>(v));
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x124>(v);
-  v += dpp_f<0x128>(v);
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x124>(v);
+  v += dpp_mov<0x128>(v);
   return v;
 }
 
