@@ -64,10 +64,10 @@ __global__ __launch_bounds__(kThreads) void grow_kernel(GrowArgs a) {
     if (kChecked) {
       // the segment's kept bytes and its whole destination inside the
       // extents (a failed bound reads from and writes to nothing outside:
-      // the chunk is skipped)
-      const bool ok = check_ok(so + pl.copy <= pl.src_ext, kChkGrowSrc) &
-                      check_ok(dof + pl.dst_bytes <= pl.dst_ext, kChkGrowDst);
-      if (!ok) continue;
+      // the chunk is skipped); both tests run, so both bits can be set
+      const bool src_ok = check_ok(so + pl.copy <= pl.src_ext, kChkGrowSrc);
+      const bool dst_ok = check_ok(dof + pl.dst_bytes <= pl.dst_ext, kChkGrowDst);
+      if (!(src_ok && dst_ok)) continue;
     }
     const uint8_t* src = pl.src + so;
     uint8_t* dst = pl.dst + dof;

@@ -420,11 +420,34 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = make_uint2(o[2 * i], o[2 * i + 1]);
       }
+    } else if constexpr (KB == 2 || KB == 4) {
+      // v_cvt_pk_u8_f32 rounds to nearest even into one byte of a word: bytes
+      // of the elements 8/KB apart, then one shift-or per byte word merges
+      // them into the packed word (element i at bits KB*i)
+      constexpr int EPW = 32 / KB, PER = 8 / KB;
+      uint32_t o[KB];
+#pragma unroll
+      for (int w = 0; w < KB; ++w) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+          uint32_t bw = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) bw = __builtin_amdgcn_cvt_pk_u8_f32(q[EPW * w + PER * k + m], k, bw);
+          acc |= bw << (KB * m);
+        }
+        o[w] = acc;
+      }
+      if (wr) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_q + orow * (D * KB / 8) + 4 * KB * g);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) dst[i] = o[i];
+      }
     } else {
       uint32_t o[KB] = {};
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const uint32_t v = (uint32_t)__builtin_rintf(q[i]);
+        const uint32_t v = __builtin_amdgcn_cvt_pk_u8_f32(q[i], 0, 0);  // RNE into byte 0
         const int bit = KB * i, wd = bit >> 5, off = bit & 31;
         o[wd] |= v << off;
         if (off + KB > 32) o[wd + 1] |= v >> (32 - off);
@@ -442,7 +465,7 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
   }
 }
 
-// Lloyd-Max indices of a group's 32 elements y for a 2-, 3- or 4-bit table,
+// Lloyd-Max indices of a group's 32 elements y for a 2- or 3-bit table,
 // packed into the group's VB words, without dividing: |y| is compared with
 // the group's thresholds RN(b * den) for the positive boundaries b.  The index
 // can then differ from that of RN(y / den) only where y / den lies within a
@@ -467,6 +490,88 @@ __device__ __forceinline__ void threshold_index(const float (&y)[32], float den,
     constexpr int nh = hi == lo ? 2 * VB : top - 32 * hi + 1;
     index_pair<VB, nh>(y[i], y[i - 1], thr, o[hi], o[lo]);
   });
+}
+
+// Lloyd-Max indices of a group's 32 elements y for the 4-bit table, through a
+// cell table held across the wave's lanes: 5 vector operations per element,
+// where the threshold search takes 12.  With zk = y * RN(4/den) the scaled
+// boundaries 4b lie at least 1.03 apart (the table's narrowest gap is 0.258).
+// Rounding y * RN(4/den) to a multiple of 1/4 (one fma with 1.5 * 2^21, whose
+// float bits then end in 4 * that multiple) and dropping the two fractional
+// bits gives the cell c; every zk in cell c lies in the closed interval
+// [c - 1/8, c + 7/8], which holds at most one scaled boundary.  Lane (c mod 64)
+// of the table holds that boundary (+1e30 where there is none) and the number
+// of boundaries below the cell, so the index #{b : 4b < zk} is
+// count + [zk > boundary], two wave permutes away; the fma's float bits serve
+// as the permute's byte address as they are (it reads lane (address / 4) mod
+// 64).  A normal den bounds |y / den| by sqrt(32) (1 + 4 ulp) -- no element
+// exceeds the root of the group's sum of squares -- so |zk| < 23 and the
+// cells -23 .. 22 fall on distinct lanes.  The index then differs from that of
+// RN(y / den) only where y / den lies within 3 ulps of a boundary (< 5e-7),
+// inside the tie window the format allows.
+struct CellTable {
+  int t;  // float bits of the cell's scaled boundary
+  int j;  // boundaries below the cell
+};
+
+template <int VB>
+__device__ __forceinline__ CellTable cell_table(int lane) {
+  const int c = lane < 32 ? lane : lane - 64;
+  const float lo = (float)c - 0.125f, hi = (float)c + 0.875f;
+  const uint32_t* bnd = boundaries<VB>();
+  float t = 1e30f;
+  int j = 0;
+  for (int k = 0; k < (1 << VB) - 1; ++k) {
+    const float b = 4.0f * __uint_as_float(bnd[k]);
+    if (b < lo) ++j;
+    else if (b <= hi) t = __builtin_fminf(t, b);
+  }
+  return {__float_as_int(t), j};
+}
+
+// Elements go from the highest down in pairs: the permutes of one pair are
+// issued before the previous pair's results are used (four pairs in flight
+// measured the same and hold 9 more registers), and each index enters its
+// word by o = (o << VB) | idx (an element that straddles two words opens the
+// lower one).
+template <int VB>
+__device__ __forceinline__ void table_index(const float (&y)[32], float rcp, const CellTable& tab,
+                                            uint32_t (&o)[VB]) {
+  constexpr int NB = 2, NBATCH = 32 / NB;
+  const float rk = 4.0f * rcp;
+  float t[2][NB];
+  int j[2][NB];
+  auto issue = [&](auto B) {
+    constexpr int b = (int)B;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int cell = __float_as_int(__builtin_fmaf(y[31 - NB * b - k], rk, 3145728.0f));
+      t[b & 1][k] = __int_as_float(__builtin_amdgcn_ds_bpermute(cell, tab.t));
+      j[b & 1][k] = __builtin_amdgcn_ds_bpermute(cell, tab.j);
+    }
+  };
+  auto consume = [&](auto B) {
+    constexpr int b = (int)B;
+    static_for<NB>([&](auto K) {
+      constexpr int i = 31 - NB * b - (int)K;
+      const uint32_t idx = (uint32_t)j[b & 1][K] + (y[i] * rk > t[b & 1][K] ? 1u : 0u);
+      constexpr int lw = (VB * i) >> 5, hw = (VB * i + VB - 1) >> 5;
+      if constexpr (lw == hw) {
+        o[lw] = (o[lw] << VB) | idx;
+      } else {
+        constexpr int nh = VB * i + VB - 32 * hw;  // bits in the higher word
+        o[hw] = (o[hw] << nh) | (idx >> (VB - nh));
+        o[lw] = idx & ((1u << (VB - nh)) - 1u);
+      }
+    });
+  };
+  static_for<NBATCH>([&](auto B) {
+    issue(B);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr ((int)B > 0) consume(std::integral_constant<int, (int)B - 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  consume(std::integral_constant<int, NBATCH - 1>{});
 }
 
 // ---------------------------------------------------------------- values
@@ -498,6 +603,8 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
     }
   }
   const float rd = inv_sqrt_d<D>();
+  [[maybe_unused]] CellTable tab{};
+  if constexpr (VB == 4) tab = cell_table<VB>(lane);
   const lds_u8* const tiles = (const lds_u8*)(tile_lds + wv * 2 * kTile);
   const bool contig = rows_contiguous(a.in, a.split);
   const bool contig_out = rows_contiguous(a.out, a.split) && !a.out_pos;
@@ -554,7 +661,16 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
 #pragma unroll
       for (int i = 0; i < 32; ++i) put(i, lloyd_max_index<VB>(y[i], bnd_lds));
     };
-    if constexpr (VB <= 4) {
+    if constexpr (VB == 4) {
+      // the permutes need every lane: the table runs wave-wide, and groups
+      // without a normal den (whose words it leaves meaningless) divide
+      table_index<VB>(y, 1.0f / den, tab, o);
+      if (!fast) {
+#pragma unroll
+        for (int i = 0; i < VB; ++i) o[i] = 0;
+        divided();
+      }
+    } else if constexpr (VB <= 4) {
       if (fast) threshold_index<VB>(y, den, o);
       else divided();
     } else {

@@ -130,6 +130,34 @@ def test_edge_values(d, kb, vb):
     check_round_trip(kt, vt, synth.sign_vector(d), kb, vb, f"edge d{d} k{kb}v{vb}")
 
 
+@pytest.mark.parametrize("kb", [2, 4, 5, 8])
+@pytest.mark.parametrize("d", [64, 256])
+def test_key_half_integers_round_to_even(d, kb):
+    """Groups whose quotients x / scale - zero are exact half-integers: every
+    group holds its minimum and maximum (scale 1, zero 0) and then every
+    half-integer between them.  Both sides compute these exactly, so the index
+    is fixed by rounding half to even alone and no tie is allowed."""
+    if kb == 8:
+        lo, hi = -127.0, 127.0
+    else:
+        lo, hi = 0.0, float((1 << kb) - 1)
+    halves = np.arange(lo, hi) + 0.5
+    rows = []
+    for r in range(8):
+        x = np.empty(d, np.float32)
+        for g in range(d // 32):
+            grp = np.resize(np.roll(halves, 7 * r + 3 * g), 32)
+            grp[0], grp[1] = lo, hi
+            x[32 * g:32 * g + 32] = np.roll(grp, r + g)
+        rows.append(x)
+    x = np.stack(rows)
+    bits = codec.f32_to_bf16(x)
+    assert np.array_equal(codec.bf16_to_f32(bits), x)          # exact in bf16
+    kt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).reshape(1, -1, 1, d)
+    st = check_round_trip(kt, kt.clone(), synth.sign_vector(d), kb, 4, f"key halves d{d} k{kb}")
+    assert st["key_ties"] == 0
+
+
 def test_strided_windows():
     """Inputs that are a head slice of a wider tensor, written into a cache
     laid out [B, H, capacity] at a token offset."""
