@@ -123,6 +123,10 @@ int32_t tq_codebook(int32_t bits, float* centroids, float* boundaries);
  *   scale and zero are stored as fp16 after the index is formed.
  * Values (same section, values bullets): y = FWHT(x*signs)/sqrt(d);
  *   scale = sqrt(mean(y^2)) per group; idx = #{boundaries < y/(scale+1e-8)}.
+ *   For 2, 3 and 4 value bits the index is found without dividing, so it may
+ *   differ by one where y/(scale+1e-8) lies within 5e-7 of a boundary (exact
+ *   equality included), inside the tie window the pages allow; 5- and 8-bit
+ *   values and all keys are exact.
  * Edge semantics: min/max propagate NaN (and order -0 below +0); round is
  * half-to-even; clip sends NaN to the low end; a constant key group gives
  * scale 0 and zero +-Inf (NaN for an all-zero group); any NaN stored as
