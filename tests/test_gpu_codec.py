@@ -158,6 +158,35 @@ def test_key_half_integers_round_to_even(d, kb):
     assert st["key_ties"] == 0
 
 
+@pytest.mark.parametrize("vb", [2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_value_spikes_reach_the_outer_cells(d, vb):
+    """Value rows whose rotation is one or two spikes: v = signs * (Hadamard row
+    k [+ c * row j]), so y = sqrt(d) (e_k + c e_j) exactly up to the 1/sqrt(d)
+    rounding.  A lone spike gives |y / den| = sqrt(32), the largest value a
+    group can hold (the outermost cells of the 4-bit table, +-22.6 after the
+    scale by 4); the other elements of its group are exact zeros, on the
+    middle boundary.  Both signs, two spikes in one group and in two groups,
+    and a spike beside a half-size one."""
+    i = np.arange(d)
+
+    def had(k):
+        return np.where(np.bitwise_count(np.bitwise_and(i, k)) % 2 == 0, 1.0, -1.0)
+
+    rng = np.random.default_rng(d + vb)
+    ks = rng.choice(d, size=6, replace=False)
+    rows = [had(ks[0]), -had(ks[1]), had(ks[2]) + had(ks[3]), had(ks[4]) - had(ks[4] ^ 1),
+            had(ks[5]) + 0.5 * had(ks[0]), -had(ks[1]) - 0.5 * had(ks[1] ^ 3)]
+    signs = synth.sign_vector(d)
+    v = np.stack(rows).astype(np.float32) * signs.astype(np.float32)
+    vbits = codec.f32_to_bf16(v)
+    assert np.array_equal(codec.bf16_to_f32(vbits), v)          # exact in bf16
+    k, _ = synth.kv_inputs("normal", 1, len(rows), 1, d, 90 + d)
+    vt = torch.from_numpy(vbits.view(np.int16)).view(torch.bfloat16).reshape(1, -1, 1, d)
+    st = check_round_trip(k, vt, signs, 8, vb, f"value spikes d{d} v{vb}")
+    assert st["value_ties"] == 0
+
+
 def test_strided_windows():
     """Inputs that are a head slice of a wider tensor, written into a cache
     laid out [B, H, capacity] at a token offset."""
