@@ -175,15 +175,24 @@ __device__ __forceinline__ void load_group(const uint16_t* p, uint32_t (&u)[16])
 // groups.  The copies are inline assembly so the compiler does not wait for
 // them before unrelated LDS reads; M0 (their LDS base) is reserved by the
 // compiler and read by no other instruction of these kernels.
+//
+// The input copies and the plane stores are non-temporal (nt): the bf16 rows
+// are read once and the planes are read by a later call, and with the decode's
+// cache copies also non-temporal this pair measured best inside the bench step
+// (quantize 561-566 against 566-569 us, the dequantize that follows 544-545
+// against 554-556 us, three alternating runs).  Either alone moves cost
+// between the kernels: non-temporal copies alone took quantize to 545 us but
+// the dequantize after it to 602 us.
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef uint32_t tq_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t tq_u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) tq_u32x4 lds_u32x4;
 constexpr int kTile = 4096;
 
 __device__ __forceinline__ int tile_slot(int reader, int q) { return 4 * reader + ((q + (reader >> 1)) & 3); }
 
 __device__ __forceinline__ void tile_copy16(const void* src, const lds_u8* dst) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"((uint32_t)(uintptr_t)dst)
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"((uint32_t)(uintptr_t)dst)
                : "memory", "m0");
 }
 
@@ -243,7 +252,7 @@ __device__ __forceinline__ void tile_issue_contig(const uint16_t* src, uint32_t 
   const uint8_t* b = reinterpret_cast<const uint8_t*>(src) + (uint64_t)base_row * (uint64_t)(2 * d);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off[j]), "s"(b),
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off[j]), "s"(b),
                  "s"((uint32_t)(uintptr_t)(stage + 1024 * j))
                  : "memory", "m0");
 }
@@ -416,9 +425,9 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
       }
       // the key plane is only 8-byte aligned: four 8-byte stores
       if (wr) {
-        uint2* dst = reinterpret_cast<uint2*>(a.k_q + orow * D + kGroup * g);
+        tq_u32x2* dst = reinterpret_cast<tq_u32x2*>(a.k_q + orow * D + kGroup * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = make_uint2(o[2 * i], o[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(tq_u32x2{o[2 * i], o[2 * i + 1]}, dst + i);
       }
     } else if constexpr (KB == 2 || KB == 4) {
       // v_cvt_pk_u8_f32 rounds to nearest even into one byte of a word: bytes
@@ -441,7 +450,7 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
       if (wr) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_q + orow * (D * KB / 8) + 4 * KB * g);
 #pragma unroll
-        for (int i = 0; i < KB; ++i) dst[i] = o[i];
+        for (int i = 0; i < KB; ++i) __builtin_nontemporal_store(o[i], dst + i);
       }
     } else {
       uint32_t o[KB] = {};
@@ -455,12 +464,12 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
       if (wr) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_q + orow * (D * KB / 8) + 4 * KB * g);
 #pragma unroll
-        for (int i = 0; i < KB; ++i) dst[i] = o[i];
+        for (int i = 0; i < KB; ++i) __builtin_nontemporal_store(o[i], dst + i);
       }
     }
     if (wr) {
-      a.k_scale[orow * G + g] = (uint16_t)f16_bits(scale);
-      a.k_zero[orow * G + g] = (uint16_t)f16_bits(zero);
+      __builtin_nontemporal_store((uint16_t)f16_bits(scale), a.k_scale + orow * G + g);
+      __builtin_nontemporal_store((uint16_t)f16_bits(zero), a.k_zero + orow * G + g);
     }
   }
 }
@@ -679,8 +688,8 @@ __device__ __forceinline__ void quantize_values_rows(const QuantArgs& a, uint32_
     if (active) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.v_q + orow * (D * VB / 8) + 4 * VB * g);
 #pragma unroll
-      for (int i = 0; i < VB; ++i) dst[i] = o[i];
-      a.v_scale[orow * G + g] = (uint16_t)f16_bits(scale);
+      for (int i = 0; i < VB; ++i) __builtin_nontemporal_store(o[i], dst + i);
+      __builtin_nontemporal_store((uint16_t)f16_bits(scale), a.v_scale + orow * G + g);
     }
   }
 }
