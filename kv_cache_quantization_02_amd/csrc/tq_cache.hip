@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
+typedef uint32_t grow_u32x4 __attribute__((ext_vector_type(4)));
 static_assert(kGrowChunkBytes == (int64_t)kThreads * 16 * kUnroll, "a chunk is one block's 16-byte units");
 
 // Plane p's descriptor by uniform selects (no dynamic index into the
@@ -74,16 +75,21 @@ __global__ __launch_bounds__(kThreads) void grow_kernel(GrowArgs a) {
     const int64_t x0 = (int64_t)chunk * kGrowChunkBytes;
     if (pl.vec16 && x0 + kGrowChunkBytes <= pl.copy) {
       // a chunk of kept rows: every load of the block issues before its
-      // first store
-      uint4 v[kUnroll];
+      // first store.  Loads and stores are non-temporal: each byte is read
+      // and written once, and keeping the copy out of the caches took the
+      // growth of the 16 x 8 x 32768 k8v3 cache from 330-336 to 273-276 us.
+      grow_u32x4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = *(const uint4*)(src + x0 + (u * kThreads + tid) * 16);
+      for (int u = 0; u < kUnroll; ++u)
+        v[u] = __builtin_nontemporal_load((const grow_u32x4*)(src + x0 + (u * kThreads + tid) * 16));
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) *(uint4*)(dst + x0 + (u * kThreads + tid) * 16) = v[u];
+      for (int u = 0; u < kUnroll; ++u)
+        __builtin_nontemporal_store(v[u], (grow_u32x4*)(dst + x0 + (u * kThreads + tid) * 16));
     } else if (pl.vec16 && x0 >= pl.copy && x0 + kGrowChunkBytes <= pl.dst_bytes) {
       // a chunk of padding
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) *(uint4*)(dst + x0 + (u * kThreads + tid) * 16) = make_uint4(0u, 0u, 0u, 0u);
+      for (int u = 0; u < kUnroll; ++u)
+        __builtin_nontemporal_store(grow_u32x4{0u, 0u, 0u, 0u}, (grow_u32x4*)(dst + x0 + (u * kThreads + tid) * 16));
     } else if (pl.vec16) {
       // the chunk where the kept rows end or the segment ends
 #pragma unroll
