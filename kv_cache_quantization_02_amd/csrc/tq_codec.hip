@@ -427,8 +427,8 @@ __device__ __forceinline__ void quantize_keys_rows(const QuantArgs& a, uint32_t 
       if constexpr (D == 128) {
         // Whole rows per store instruction.  Each lane's four 8-byte stores
         // of its group (8 bytes at a 32-byte stride per instruction) reach
-        // memory as partial lines when they bypass the caches: 7% more bytes
-        // written per launch, and 25 us.  The wave's 16 code rows (2 KB, row
+        // memory as partial lines when they bypass the caches (7% more bytes
+        // written per launch).  The wave's 16 code rows (2 KB, row
         // r at 128 r, group g at 32 g) and their plane rows are staged in this
         // iteration's input tile, already read into registers, and store j
         // writes rows 4 j .. 4 j + 3 whole: lane L takes bytes 8 (L mod 16) of
